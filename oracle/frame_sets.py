@@ -109,21 +109,26 @@ def frame_set_for(policy: dict, Tq: int, Tk: int, offset: int, chunk: int, tq: i
 
     policy keys: kind, n_sink, window, budget, t_per, step, topk, n_recent, lo, hi.
     `selected` holds the top-k frames of this query frame's group (MEMORY only).
+    Every set is a subset of the existing frames {0..Tk-1} [LVSA §2: A(t)
+    replaces the full set {0, ..., T-1}], so a sink longer than the cache is cut.
     """
     kind = policy["kind"]
     if kind == FULL:
-        return full(Tk)
-    if kind == LVSA:
-        return lvsa(Tk, policy["budget"], policy["window"], policy["t_per"],
-                    policy["step"], offset + tq)
-    e = chunk_last_frame(tq, chunk, offset)
-    if kind == SINK_WINDOW:
-        return sink_window(policy["n_sink"], policy["window"], e)
-    if kind == MEMORY:
-        return memory(selected, policy["n_recent"], e)
-    if kind == RANGE:
-        return frame_range(policy["lo"], policy["hi"], Tk)
-    raise ValueError(f"unknown policy kind {kind}")
+        frames = full(Tk)
+    elif kind == LVSA:
+        frames = lvsa(Tk, policy["budget"], policy["window"], policy["t_per"],
+                      policy["step"], offset + tq)
+    else:
+        e = chunk_last_frame(tq, chunk, offset)
+        if kind == SINK_WINDOW:
+            frames = sink_window(policy["n_sink"], policy["window"], e)
+        elif kind == MEMORY:
+            frames = memory(selected, policy["n_recent"], e)
+        elif kind == RANGE:
+            frames = frame_range(policy["lo"], policy["hi"], Tk)
+        else:
+            raise ValueError(f"unknown policy kind {kind}")
+    return [f for f in frames if 0 <= f < Tk]
 
 
 def build(policies: list[dict], B: int, Tq: int, Tk: int, offset: int = 0,
