@@ -1,0 +1,279 @@
+"""Python binding of libfsa (frame-block-sparse softmax attention on MI355X).
+
+A thin ctypes layer over the C ABI declared in include/fsa.h: it checks
+tensor dtypes/shapes, allocates outputs and workspaces with torch on the
+inputs' device, passes raw pointers and torch's current HIP stream, and turns
+a non-OK status into FsaError.  Every computation happens in the library's HIP
+kernels; there is no fallback.  Importing this module fails loudly when
+libfsa.so has not been built (python -m frame_sparse_attention_amd.build).
+
+Functions (same names as the C entry points, without the fsa_ prefix):
+  frame_set_capacity, build_frame_sets, build_frame_sets_host,
+  validate_frame_sets, select_topk_frames, sparse_frame_attn, merge_lse,
+  plus the workspace-size queries, abi_version and last_error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsa.so")
+
+FULL, LVSA, SINK_WINDOW, MEMORY, RANGE = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+MAX_HEADS = 64
+MAX_CAP = 1024
+
+STATUS_NAMES = {0: "FSA_OK", 1: "FSA_E_ARG", 2: "FSA_E_SHAPE", 3: "FSA_E_DTYPE",
+                4: "FSA_E_CAPACITY", 5: "FSA_E_LIST", 6: "FSA_E_HIP"}
+
+
+class FsaError(RuntimeError):
+    """A libfsa call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class HeadPolicy(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("kind", "n_sink", "window", "budget", "t_per", "step", "topk", "n_recent",
+                 "lo", "hi")]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m frame_sparse_attention_amd.build` (needs ROCm hipcc)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t,
+                              ctypes.c_void_p)
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+_psz = ctypes.POINTER(ctypes.c_size_t)
+_ppol = ctypes.POINTER(HeadPolicy)
+
+_SIGS = {
+    "fsa_abi_version": (_i32, []),
+    "fsa_last_error": (ctypes.c_char_p, []),
+    "fsa_frame_set_capacity": (_i32, [_i32, _ppol, _i32, _i32, _i32, _i32, _pi32]),
+    "fsa_build_frame_sets": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _ppol, _vp, _i32, _i32,
+                                    _vp, _vp, _vp]),
+    "fsa_build_frame_sets_host": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _ppol, _vp, _i32,
+                                         _i32, _vp, _vp]),
+    "fsa_validate_frame_sets": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "fsa_select_topk_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              _psz]),
+    "fsa_select_topk_frames": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "fsa_sparse_frame_attn_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _psz]),
+    "fsa_sparse_frame_attn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "fsa_merge_lse": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def abi_version() -> int:
+    return int(_lib.fsa_abi_version())
+
+
+def last_error() -> str:
+    return _lib.fsa_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FsaError(status, last_error())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _policies(policies) -> ctypes.Array:
+    arr = (HeadPolicy * max(1, len(policies)))()
+    for i, p in enumerate(policies):
+        for name, _ in HeadPolicy._fields_:
+            setattr(arr[i], name, int(p.get(name, 0 if name != "t_per" else 1)))
+    return arr
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need_contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# ----------------------------------------------------------------------------- frame sets
+def frame_set_capacity(policies, Tq: int, Tk: int, offset: int = 0, chunk: int = 1) -> int:
+    """Smallest cap that holds every frame set the policies can produce."""
+    out = ctypes.c_int32(0)
+    _check(_lib.fsa_frame_set_capacity(len(policies), _policies(policies), Tq, Tk, offset, chunk,
+                                       ctypes.byref(out)))
+    return out.value
+
+
+def build_frame_sets(policies, B: int, Tq: int, Tk: int, offset: int = 0, chunk: int = 1,
+                     selected: torch.Tensor | None = None, cap: int | None = None,
+                     device="cuda"):
+    """Frame sets of every (b, h, tq) on the device: (idx [B,H,Tq,cap], cnt [B,H,Tq]) int32.
+
+    selected: device int32 [B, H, Tq // chunk, k] frames chosen per query group
+    (read for MEMORY heads only)."""
+    H = len(policies)
+    if cap is None:
+        cap = frame_set_capacity(policies, Tq, Tk, offset, chunk)
+    idx = torch.empty((B, H, Tq, cap), dtype=torch.int32, device=device)
+    cnt = torch.empty((B, H, Tq), dtype=torch.int32, device=device)
+    topk_k = 0
+    if selected is not None:
+        if selected.dtype != torch.int32 or selected.dim() != 4:
+            raise ValueError("selected must be int32 [B, H, groups, k]")
+        _need_contig(selected)
+        topk_k = selected.shape[3]
+    _check(_lib.fsa_build_frame_sets(B, H, Tq, Tk, offset, chunk, _policies(policies),
+                                     _ptr(selected), topk_k, cap, _ptr(idx), _ptr(cnt),
+                                     _stream(idx.device)))
+    return idx, cnt
+
+
+def build_frame_sets_host(policies, B: int, Tq: int, Tk: int, offset: int = 0, chunk: int = 1,
+                          selected: np.ndarray | None = None, cap: int | None = None):
+    """The same construction on host arrays (numpy int32)."""
+    H = len(policies)
+    if cap is None:
+        cap = frame_set_capacity(policies, Tq, Tk, offset, chunk)
+    idx = np.empty((B, H, Tq, cap), dtype=np.int32)
+    cnt = np.empty((B, H, Tq), dtype=np.int32)
+    topk_k = 0
+    if selected is not None:
+        selected = np.ascontiguousarray(selected, dtype=np.int32)
+        topk_k = selected.shape[3]
+    _check(_lib.fsa_build_frame_sets_host(B, H, Tq, Tk, offset, chunk, _policies(policies),
+                                          _ptr(selected), topk_k, cap, _ptr(idx), _ptr(cnt)))
+    return idx, cnt
+
+
+def validate_frame_sets(idx, cnt, Tk: int) -> None:
+    """Raises FsaError (FSA_E_LIST) unless every list is sorted, unique and in range."""
+    idx = np.ascontiguousarray(idx.cpu().numpy() if torch.is_tensor(idx) else idx, dtype=np.int32)
+    cnt = np.ascontiguousarray(cnt.cpu().numpy() if torch.is_tensor(cnt) else cnt, dtype=np.int32)
+    B, H, Tq, cap = idx.shape
+    _check(_lib.fsa_validate_frame_sets(B, H, Tq, Tk, cap, _ptr(idx), _ptr(cnt)))
+
+
+# ----------------------------------------------------------------------------- top-k
+def select_topk_frames(q: torch.Tensor, k: torch.Tensor, P: int, h_begin: int, h_end: int,
+                       q_group: int, cand_begin: int, cand_end: int, topk: int,
+                       return_scores: bool = False, out: torch.Tensor | None = None):
+    """Top-k frames by pooled Q.K per (b, h in [h_begin, h_end), query group).
+
+    Returns int32 [B, H, G, topk] (rows of other heads are -1, or left as in
+    `out`), and float64 scores [B, H, G, cand_end - cand_begin] when asked."""
+    _need_contig(q, k)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    G = Nq // (q_group * P) if q_group * P > 0 else 0
+    if out is None:
+        out = torch.full((B, H, G, topk), -1, dtype=torch.int32, device=q.device)
+    scores = None
+    if return_scores:
+        scores = torch.full((B, H, G, cand_end - cand_begin), float("nan"), dtype=torch.float64,
+                            device=q.device)
+    nbytes = ctypes.c_size_t(0)
+    _check(_lib.fsa_select_topk_workspace_size(B, H, Nq, D, P, q_group, cand_begin, cand_end,
+                                               ctypes.byref(nbytes)))
+    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)
+    _check(_lib.fsa_select_topk_frames(_ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P,
+                                       h_begin, h_end, q_group, cand_begin, cand_end, topk,
+                                       _ptr(out), _ptr(scores), _ptr(ws), nbytes.value,
+                                       _stream(q.device)))
+    return (out, scores) if return_scores else out
+
+
+# ----------------------------------------------------------------------------- attention
+def sparse_frame_attn_workspace_size(dtype, B: int, H: int, Nk: int, D: int) -> int:
+    code = dtype if isinstance(dtype, int) else (BF16 if dtype == torch.bfloat16 else F32)
+    out = ctypes.c_size_t(0)
+    _check(_lib.fsa_sparse_frame_attn_workspace_size(code, B, H, Nk, D, ctypes.byref(out)))
+    return out.value
+
+
+def sparse_frame_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                      cnt: torch.Tensor, P: int, scale: float | None = None,
+                      workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                      out_lse: torch.Tensor | None = None):
+    """Frame-sparse attention: returns (O float32 [B,H,Nq,D], LSE float32 [B,H,Nq])."""
+    _need_contig(q, k, v, idx, cnt)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if idx.dtype != torch.int32 or cnt.dtype != torch.int32:
+        raise TypeError("idx and cnt must be int32")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
+        raise ValueError("k and v must be [B, H, Nk, D] matching q")
+    if idx.dim() != 4 or idx.shape[:2] != (B, H) or cnt.shape != idx.shape[:3]:
+        raise ValueError("idx must be [B,H,Tq,cap] and cnt [B,H,Tq]")
+    if P > 0 and idx.shape[2] != Nq // P:
+        raise ValueError("idx has the wrong number of query frames")
+    dt = _dtype_code(q)
+    o = out if out is not None else torch.empty((B, H, Nq, D), dtype=torch.float32,
+                                                device=q.device)
+    lse = out_lse if out_lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
+                                                          device=q.device)
+    need = sparse_frame_attn_workspace_size(dt, B, H, Nk, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.fsa_sparse_frame_attn(_ptr(q), _ptr(k), _ptr(v), dt, B, H, Nq, Nk, D, P,
+                                      _ptr(idx), _ptr(cnt), idx.shape[3],
+                                      float(scale) if scale is not None else 0.0, _ptr(o),
+                                      _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device)))
+    return o, lse
+
+
+def merge_lse(o1: torch.Tensor, lse1: torch.Tensor, o2: torch.Tensor, lse2: torch.Tensor,
+              out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None):
+    """Exact LSE merge of two partial attentions (float32); returns (O, LSE)."""
+    _need_contig(o1, lse1, o2, lse2)
+    if o1.shape != o2.shape or lse1.shape != lse2.shape or o1.shape[:-1] != lse1.shape:
+        raise ValueError("o1/o2 must be [..., D] and lse1/lse2 the matching [...]")
+    for t in (o1, lse1, o2, lse2):
+        if t.dtype != torch.float32:
+            raise TypeError("merge_lse works on float32 tensors")
+    D = o1.shape[-1]
+    rows = lse1.numel()
+    o = out if out is not None else torch.empty_like(o1)
+    lse = out_lse if out_lse is not None else torch.empty_like(lse1)
+    _check(_lib.fsa_merge_lse(_ptr(o1), _ptr(lse1), _ptr(o2), _ptr(lse2), rows, D, _ptr(o),
+                              _ptr(lse), _stream(o1.device)))
+    return o, lse

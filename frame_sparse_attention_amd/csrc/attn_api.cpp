@@ -1,0 +1,72 @@
+// C entry points of the sparse frame attention: argument validation and
+// dispatch to the float32 or the bfloat16 (matrix-core) kernels.
+#include <cmath>
+
+#include "fsa_internal.h"
+
+namespace fsa {
+fsa_status launch_attn_f32(const float *q, const float *k, const float *v, const int32_t *idx,
+                           const int32_t *cnt, int cap, int B, int H, int Nq, int Nk, int D,
+                           int P, float scale, float *o, float *lse, hipStream_t stream);
+fsa_status launch_attn_bf16(const void *q, const void *k, const void *v, const int32_t *idx,
+                            const int32_t *cnt, int cap, int B, int H, int Nq, int Nk, int D,
+                            int P, float scale, float *o, float *lse, void *workspace,
+                            hipStream_t stream);
+size_t attn_bf16_workspace(long long heads, int Nk, int D);
+}  // namespace fsa
+
+namespace {
+
+fsa_status check_common(int32_t dt, int32_t B, int32_t H, int32_t Nk, int32_t D) {
+  FSA_REQUIRE(dt == FSA_F32 || dt == FSA_BF16, FSA_E_DTYPE, "unknown dtype %d", dt);
+  FSA_REQUIRE(D == 64 || D == 128, FSA_E_DTYPE, "head_dim D=%d is not 64 or 128", D);
+  FSA_REQUIRE(B >= 0 && H >= 0 && Nk >= 0, FSA_E_ARG, "negative size (B=%d H=%d Nk=%d)", B, H,
+              Nk);
+  return FSA_OK;
+}
+
+}  // namespace
+
+extern "C" fsa_status fsa_sparse_frame_attn_workspace_size(int32_t dt, int32_t B, int32_t H,
+                                                           int32_t Nk, int32_t D,
+                                                           size_t *bytes) {
+  fsa::clear_error();
+  FSA_REQUIRE(bytes != nullptr, FSA_E_ARG, "bytes is NULL");
+  fsa_status st = check_common(dt, B, H, Nk, D);
+  if (st != FSA_OK) return st;
+  *bytes = dt == FSA_BF16 ? fsa::attn_bf16_workspace((long long)B * H, Nk, D) : 0;
+  return FSA_OK;
+}
+
+extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const void *v,
+                                            int32_t dt, int32_t B, int32_t H, int32_t Nq,
+                                            int32_t Nk, int32_t D, int32_t P, const int32_t *idx,
+                                            const int32_t *cnt, int32_t cap, float scale,
+                                            float *o, float *lse, void *workspace,
+                                            size_t workspace_bytes, void *stream) {
+  fsa::clear_error();
+  fsa_status st = check_common(dt, B, H, Nk, D);
+  if (st != FSA_OK) return st;
+  FSA_REQUIRE(Nq >= 0, FSA_E_ARG, "Nq=%d must be >= 0", Nq);
+  FSA_REQUIRE(P >= 1, FSA_E_SHAPE, "P=%d must be >= 1", P);
+  FSA_REQUIRE(Nq % P == 0, FSA_E_SHAPE, "Nq=%d is not a multiple of P=%d", Nq, P);
+  FSA_REQUIRE(Nk % P == 0, FSA_E_SHAPE, "Nk=%d is not a multiple of P=%d", Nk, P);
+  FSA_REQUIRE(cap >= 1 && cap <= FSA_MAX_CAP, FSA_E_CAPACITY, "cap=%d outside [1, %d]", cap,
+              FSA_MAX_CAP);
+  FSA_REQUIRE(std::isfinite(scale), FSA_E_ARG, "scale is not finite");
+  if ((long long)B * H * Nq == 0) return FSA_OK;
+  FSA_REQUIRE(q && o && lse && idx && cnt, FSA_E_ARG, "null pointer argument");
+  FSA_REQUIRE(Nk == 0 || (k && v), FSA_E_ARG, "k or v is NULL");
+  if (scale <= 0.f) scale = 1.f / std::sqrt((float)D);
+  hipStream_t s = fsa::as_stream(stream);
+  if (dt == FSA_F32)
+    return fsa::launch_attn_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+                                static_cast<const float *>(v), idx, cnt, cap, B, H, Nq, Nk, D,
+                                P, scale, o, lse, s);
+  const size_t need = fsa::attn_bf16_workspace((long long)B * H, Nk, D);
+  FSA_REQUIRE(need == 0 || workspace != nullptr, FSA_E_ARG, "workspace is NULL");
+  FSA_REQUIRE(workspace_bytes >= need, FSA_E_CAPACITY, "workspace of %zu bytes < %zu needed",
+              workspace_bytes, need);
+  return fsa::launch_attn_bf16(q, k, v, idx, cnt, cap, B, H, Nq, Nk, D, P, scale, o, lse,
+                               workspace, s);
+}

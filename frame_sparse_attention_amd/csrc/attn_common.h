@@ -1,0 +1,68 @@
+// Device helpers shared by the attention kernels: turning a frame list into
+// runs of consecutive frames, and the XCD-aware tile order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fsa_internal.h"
+
+namespace fsa {
+
+// Runs of consecutive frames of one list, in LDS: run r covers frames
+// run_lo[r] .. run_hi[r].  Consecutive frames are contiguous in memory
+// (token n = f*P + p), so one run is one contiguous key range and the tile
+// loop walks it without per-frame tails (LVSA §2: the attended set is a union
+// of an interval and the anchors, so a list of 21-33 frames is 5-15 runs).
+struct RunList {
+  int *lo;
+  int *hi;
+};
+
+// Builds the runs of list[0..n) (n clamped to [0, cap]) with wavefront 0 of
+// the block; entries outside [0, Tk) are skipped.  Returns the run count to
+// every thread (after a block barrier).  `s_count` is one LDS int.
+__device__ inline int build_runs(const int32_t *__restrict__ list, int n, int cap, int Tk,
+                                 RunList runs, int *s_count) {
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    int carry = 0;
+    for (int base = 0; base < n; base += 64) {
+      const int i = base + lane;
+      const int f = i < n ? list[i] : -1;
+      const int fp = (i < n && i > 0) ? list[i - 1] : -1;
+      const int fn = (i + 1 < n) ? list[i + 1] : -1;
+      const bool valid = i < n && f >= 0 && f < Tk;
+      const bool pvalid = fp >= 0 && fp < Tk;
+      const bool nvalid = fn >= 0 && fn < Tk;
+      const bool starts = valid && !(pvalid && fp == f - 1);
+      const bool ends = valid && !(nvalid && fn == f + 1);
+      const uint64_t smask = __ballot(starts);
+      const int before = carry + __popcll(smask & lt);
+      if (starts) runs.lo[before] = f;
+      // the run an entry belongs to is the one opened by the latest start at or before it
+      if (ends) runs.hi[before + (starts ? 1 : 0) - 1] = f;
+      carry += __popcll(smask);
+    }
+    if (lane == 0) *s_count = carry;
+  }
+  __syncthreads();
+  return *s_count;
+}
+
+// Maps the hardware block id to a logical tile id so that consecutive
+// logical tiles run on the same XCD.  Blocks are dealt to the 8 XCDs of an
+// MI355X round-robin (block b on XCD b % 8); each XCD gets one contiguous
+// range of logical tiles, so the query tiles of one (head, frame) -- which
+// read the same K/V frames -- share that XCD's L2.
+__device__ inline int xcd_logical_tile(int bid, int nblk) {
+  constexpr int kXcd = 8;
+  const int per = nblk / kXcd, rem = nblk % kXcd;
+  const int xcd = bid % kXcd, local = bid / kXcd;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+}  // namespace fsa

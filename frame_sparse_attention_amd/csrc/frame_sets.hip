@@ -1,0 +1,306 @@
+// Frame-set construction: the KV frames A(t) each query frame attends to.
+//
+// Policies follow LVSA §2 core mechanism (rotating global anchors united with
+// a local window that is widened until |A(t)| reaches the budget C), Head
+// Forcing methodology §2 (local, anchor and memory heads) and ISPA §2 item 1
+// (local stream = current chunk + sink frame).  The arithmetic is integer
+// only; the same routine runs in the device kernel (one thread per query
+// frame) and in the host entry point.
+#include <algorithm>
+
+#include "fsa_internal.h"
+
+namespace {
+
+struct PolicyArray {
+  fsa_head_policy p[FSA_MAX_HEADS];
+};
+
+__host__ __device__ inline int pos_mod(int a, int m) {
+  int r = a % m;
+  return r < 0 ? r + m : r;
+}
+
+// LVSA window for query frame t: returns the inclusive interval [lo, hi]
+// (hi < lo when empty) of the nearest frames, grown from min(W, T) frames
+// until anchors ∪ window holds min(C, T) frames.  Frames join the window in
+// the order of (|f - t|, f): t, t-1, t+1, t-2, ... with the earlier frame
+// first on ties; at an end of the video the other side keeps growing.
+__host__ __device__ inline void lvsa_window(int T, int C, int W, int t_per, int r, int t,
+                                            int *lo_out, int *hi_out) {
+  int n_anchor = r < T ? (T - 1 - r) / t_per + 1 : 0;
+  int target = C < T ? C : T;
+  int base = W < T ? W : T;
+  int lo = t, hi = t - 1;  // empty
+  int size = 0, uni = n_anchor;
+  while (size < T && (size < base || uni < target)) {
+    int f;
+    if (size == 0) {
+      f = t;
+      lo = hi = t;
+    } else {
+      int left = lo - 1, right = hi + 1;
+      bool take_left = left >= 0 && (right >= T || (t - left) <= (right - t));
+      if (take_left) {
+        f = left;
+        lo = left;
+      } else {
+        f = right;
+        hi = right;
+      }
+    }
+    ++size;
+    if (pos_mod(f, t_per) != r) ++uni;
+  }
+  *lo_out = lo;
+  *hi_out = hi;
+}
+
+// Frame set of query frame tq under one policy.  Writes at most `cap`
+// entries to out (ascending), pads the rest of the row with -1 and returns the
+// number of frames written.  `sel` holds the group's selected frames (MEMORY
+// heads read the first pol.topk of them).
+__host__ __device__ inline int build_one(const fsa_head_policy &pol, int Tk, int offset,
+                                         int chunk, int tq, const int32_t *sel, int cap,
+                                         int32_t *out) {
+  int n = 0;
+  const int e = offset + (tq / chunk + 1) * chunk - 1;  // last KV frame of tq's chunk
+  switch (pol.kind) {
+    case FSA_POL_FULL:
+      for (int f = 0; f < Tk && n < cap; ++f) out[n++] = f;
+      break;
+    case FSA_POL_LVSA: {
+      const int r = pos_mod(pol.step, pol.t_per);
+      int lo, hi;
+      lvsa_window(Tk, pol.budget, pol.window, pol.t_per, r, offset + tq, &lo, &hi);
+      for (int f = 0; f < Tk && n < cap; ++f)
+        if ((f >= lo && f <= hi) || pos_mod(f, pol.t_per) == r) out[n++] = f;
+      break;
+    }
+    case FSA_POL_SINK_WINDOW: {
+      const int wlo = e - pol.window + 1;
+      for (int f = 0; f < Tk && n < cap; ++f)
+        if (f < pol.n_sink || (f >= wlo && f <= e)) out[n++] = f;
+      break;
+    }
+    case FSA_POL_MEMORY: {
+      const int rlo = e - pol.n_recent + 1;
+      for (int f = 0; f < Tk && n < cap; ++f) {
+        bool keep = f >= rlo && f <= e;
+        for (int j = 0; j < pol.topk && !keep; ++j) keep = sel[j] == f;
+        if (keep) out[n++] = f;
+      }
+      break;
+    }
+    case FSA_POL_RANGE:
+      for (int f = pol.lo < 0 ? 0 : pol.lo; f <= pol.hi && f < Tk && n < cap; ++f) out[n++] = f;
+      break;
+    default:
+      break;
+  }
+  for (int j = n; j < cap; ++j) out[j] = -1;
+  return n;
+}
+
+__global__ void build_frame_sets_kernel(int B, int H, int Tq, int Tk, int offset, int chunk,
+                                        PolicyArray pols, const int32_t *__restrict__ selected,
+                                        int topk_k, int cap, int32_t *__restrict__ idx,
+                                        int32_t *__restrict__ cnt) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)B * H * Tq;
+  if (i >= total) return;
+  const int tq = (int)(i % Tq);
+  const int h = (int)((i / Tq) % H);
+  const int b = (int)(i / ((long long)Tq * H));
+  const fsa_head_policy &pol = pols.p[h];
+  const int groups = Tq / chunk;
+  const int32_t *sel = nullptr;
+  if (pol.kind == FSA_POL_MEMORY)
+    sel = selected + (((long long)b * H + h) * groups + tq / chunk) * topk_k;
+  cnt[i] = build_one(pol, Tk, offset, chunk, tq, sel, cap, idx + i * cap);
+}
+
+fsa_status policy_capacity(const fsa_head_policy &p, int Tq, int Tk, int offset, int chunk,
+                           int *need) {
+  (void)Tq;
+  (void)chunk;
+  (void)offset;
+  switch (p.kind) {
+    case FSA_POL_FULL:
+      *need = Tk;
+      break;
+    case FSA_POL_LVSA: {
+      if (p.t_per < 1) return fsa::fail(FSA_E_ARG, "t_per=%d must be >= 1", p.t_per);
+      int r = pos_mod(p.step, p.t_per);
+      int n_anchor = r < Tk ? (Tk - 1 - r) / p.t_per + 1 : 0;
+      int c = std::min(p.budget, Tk);
+      int w = n_anchor + std::min(p.window, Tk);
+      *need = std::min(Tk, std::max(c, w));
+      break;
+    }
+    case FSA_POL_SINK_WINDOW:
+      *need = std::min(Tk, std::min(p.n_sink, Tk) + std::min(p.window, Tk));
+      break;
+    case FSA_POL_MEMORY:
+      *need = std::min(Tk, p.topk + p.n_recent);
+      break;
+    case FSA_POL_RANGE: {
+      int lo = std::max(0, p.lo), hi = std::min(p.hi, Tk - 1);
+      *need = hi >= lo ? hi - lo + 1 : 0;
+      break;
+    }
+    default:
+      return fsa::fail(FSA_E_ARG, "unknown policy kind %d", p.kind);
+  }
+  return FSA_OK;
+}
+
+fsa_status check_policies(int32_t B, int32_t H, int32_t Tq, int32_t Tk, int32_t offset,
+                          int32_t chunk, const fsa_head_policy *pol, int32_t topk_k,
+                          bool have_selected, int32_t cap, bool check_cap) {
+  FSA_REQUIRE(B >= 0 && H >= 0 && Tq >= 0 && Tk >= 0, FSA_E_ARG,
+              "negative size (B=%d H=%d Tq=%d Tk=%d)", B, H, Tq, Tk);
+  FSA_REQUIRE(H <= FSA_MAX_HEADS, FSA_E_ARG, "H=%d exceeds FSA_MAX_HEADS=%d", H,
+              FSA_MAX_HEADS);
+  FSA_REQUIRE(H == 0 || pol != nullptr, FSA_E_ARG, "policies is NULL");
+  FSA_REQUIRE(chunk >= 1, FSA_E_ARG, "chunk=%d must be >= 1", chunk);
+  FSA_REQUIRE(Tq % chunk == 0, FSA_E_ARG, "Tq=%d is not a multiple of chunk=%d", Tq, chunk);
+  FSA_REQUIRE(offset >= 0, FSA_E_ARG, "offset=%d must be >= 0", offset);
+  FSA_REQUIRE(cap >= 1 && cap <= FSA_MAX_CAP, FSA_E_CAPACITY, "cap=%d outside [1, %d]", cap,
+              FSA_MAX_CAP);
+  for (int h = 0; h < H; ++h) {
+    const fsa_head_policy &p = pol[h];
+    switch (p.kind) {
+      case FSA_POL_FULL:
+      case FSA_POL_RANGE:
+        break;
+      case FSA_POL_LVSA:
+        FSA_REQUIRE(p.t_per >= 1, FSA_E_ARG, "head %d: t_per=%d must be >= 1", h, p.t_per);
+        FSA_REQUIRE(p.window >= 0 && p.budget >= 0, FSA_E_ARG,
+                    "head %d: window=%d and budget=%d must be >= 0", h, p.window, p.budget);
+        FSA_REQUIRE(offset + Tq <= Tk, FSA_E_ARG,
+                    "head %d: query frames offset+Tq=%d exceed Tk=%d", h, offset + Tq, Tk);
+        break;
+      case FSA_POL_SINK_WINDOW:
+        FSA_REQUIRE(p.window >= 0 && p.n_sink >= 0, FSA_E_ARG,
+                    "head %d: window=%d and n_sink=%d must be >= 0", h, p.window, p.n_sink);
+        FSA_REQUIRE(offset + Tq <= Tk, FSA_E_ARG,
+                    "head %d: query chunk end offset+Tq=%d exceeds Tk=%d", h, offset + Tq, Tk);
+        break;
+      case FSA_POL_MEMORY:
+        FSA_REQUIRE(p.n_recent >= 0 && p.topk >= 0, FSA_E_ARG,
+                    "head %d: n_recent=%d and topk=%d must be >= 0", h, p.n_recent, p.topk);
+        FSA_REQUIRE(have_selected, FSA_E_ARG, "head %d is MEMORY but selected is NULL", h);
+        FSA_REQUIRE(p.topk <= topk_k, FSA_E_ARG,
+                    "head %d: topk=%d exceeds the %d selected frames per group", h, p.topk,
+                    topk_k);
+        FSA_REQUIRE(offset + Tq <= Tk, FSA_E_ARG,
+                    "head %d: query chunk end offset+Tq=%d exceeds Tk=%d", h, offset + Tq, Tk);
+        break;
+      default:
+        return fsa::fail(FSA_E_ARG, "head %d: unknown policy kind %d", h, p.kind);
+    }
+    if (check_cap) {
+      int need = 0;
+      fsa_status st = policy_capacity(p, Tq, Tk, offset, chunk, &need);
+      if (st != FSA_OK) return st;
+      FSA_REQUIRE(need <= cap, FSA_E_CAPACITY, "head %d needs cap >= %d, got %d", h, need, cap);
+    }
+  }
+  return FSA_OK;
+}
+
+}  // namespace
+
+extern "C" fsa_status fsa_frame_set_capacity(int32_t H, const fsa_head_policy *policies,
+                                             int32_t Tq, int32_t Tk, int32_t offset,
+                                             int32_t chunk, int32_t *cap_out) {
+  fsa::clear_error();
+  FSA_REQUIRE(cap_out != nullptr, FSA_E_ARG, "cap_out is NULL");
+  FSA_REQUIRE(H >= 0 && H <= FSA_MAX_HEADS, FSA_E_ARG, "H=%d outside [0, %d]", H, FSA_MAX_HEADS);
+  FSA_REQUIRE(H == 0 || policies != nullptr, FSA_E_ARG, "policies is NULL");
+  FSA_REQUIRE(Tk >= 0, FSA_E_ARG, "Tk=%d must be >= 0", Tk);
+  int cap = 1;
+  for (int h = 0; h < H; ++h) {
+    int need = 0;
+    fsa_status st = policy_capacity(policies[h], Tq, Tk, offset, chunk, &need);
+    if (st != FSA_OK) return st;
+    cap = std::max(cap, need);
+  }
+  *cap_out = cap;
+  return FSA_OK;
+}
+
+extern "C" fsa_status fsa_build_frame_sets(int32_t B, int32_t H, int32_t Tq, int32_t Tk,
+                                           int32_t offset, int32_t chunk,
+                                           const fsa_head_policy *policies,
+                                           const int32_t *selected, int32_t topk_k, int32_t cap,
+                                           int32_t *idx, int32_t *cnt, void *stream) {
+  fsa::clear_error();
+  fsa_status st = check_policies(B, H, Tq, Tk, offset, chunk, policies, topk_k,
+                                 selected != nullptr, cap, true);
+  if (st != FSA_OK) return st;
+  const long long total = (long long)B * H * Tq;
+  if (total == 0) return FSA_OK;
+  FSA_REQUIRE(idx != nullptr && cnt != nullptr, FSA_E_ARG, "idx or cnt is NULL");
+  PolicyArray arr{};
+  for (int h = 0; h < H; ++h) arr.p[h] = policies[h];
+  const int threads = 64;
+  const long long blocks = (total + threads - 1) / threads;
+  FSA_REQUIRE(blocks < (1LL << 31), FSA_E_ARG, "too many query frames (%lld)", total);
+  hipLaunchKernelGGL(build_frame_sets_kernel, dim3((unsigned)blocks), dim3(threads), 0,
+                     fsa::as_stream(stream), B, H, Tq, Tk, offset, chunk, arr, selected,
+                     topk_k, cap, idx, cnt);
+  return fsa::check_launch("build_frame_sets");
+}
+
+extern "C" fsa_status fsa_build_frame_sets_host(int32_t B, int32_t H, int32_t Tq, int32_t Tk,
+                                                int32_t offset, int32_t chunk,
+                                                const fsa_head_policy *policies,
+                                                const int32_t *selected, int32_t topk_k,
+                                                int32_t cap, int32_t *idx, int32_t *cnt) {
+  fsa::clear_error();
+  fsa_status st = check_policies(B, H, Tq, Tk, offset, chunk, policies, topk_k,
+                                 selected != nullptr, cap, true);
+  if (st != FSA_OK) return st;
+  const long long total = (long long)B * H * Tq;
+  if (total == 0) return FSA_OK;
+  FSA_REQUIRE(idx != nullptr && cnt != nullptr, FSA_E_ARG, "idx or cnt is NULL");
+  const int groups = Tq / chunk;
+  for (long long i = 0; i < total; ++i) {
+    const int tq = (int)(i % Tq);
+    const int h = (int)((i / Tq) % H);
+    const int b = (int)(i / ((long long)Tq * H));
+    const fsa_head_policy &pol = policies[h];
+    const int32_t *sel = nullptr;
+    if (pol.kind == FSA_POL_MEMORY)
+      sel = selected + (((long long)b * H + h) * groups + tq / chunk) * topk_k;
+    cnt[i] = build_one(pol, Tk, offset, chunk, tq, sel, cap, idx + i * cap);
+  }
+  return FSA_OK;
+}
+
+extern "C" fsa_status fsa_validate_frame_sets(int32_t B, int32_t H, int32_t Tq, int32_t Tk,
+                                              int32_t cap, const int32_t *idx,
+                                              const int32_t *cnt) {
+  fsa::clear_error();
+  FSA_REQUIRE(B >= 0 && H >= 0 && Tq >= 0 && Tk >= 0 && cap >= 1, FSA_E_ARG,
+              "bad sizes (B=%d H=%d Tq=%d Tk=%d cap=%d)", B, H, Tq, Tk, cap);
+  const long long total = (long long)B * H * Tq;
+  if (total == 0) return FSA_OK;
+  FSA_REQUIRE(idx != nullptr && cnt != nullptr, FSA_E_ARG, "idx or cnt is NULL");
+  for (long long i = 0; i < total; ++i) {
+    const int tq = (int)(i % Tq), h = (int)((i / Tq) % H), b = (int)(i / ((long long)Tq * H));
+    const int n = cnt[i];
+    FSA_REQUIRE(n >= 0 && n <= cap, FSA_E_LIST, "(b=%d,h=%d,t=%d): cnt=%d outside [0, %d]", b, h,
+                tq, n, cap);
+    for (int j = 0; j < n; ++j) {
+      const int f = idx[i * cap + j];
+      FSA_REQUIRE(f >= 0 && f < Tk, FSA_E_LIST, "(b=%d,h=%d,t=%d): entry %d = %d outside [0, %d)",
+                  b, h, tq, j, f, Tk);
+      FSA_REQUIRE(j == 0 || f > idx[i * cap + j - 1], FSA_E_LIST,
+                  "(b=%d,h=%d,t=%d): entry %d = %d not above the previous entry", b, h, tq, j, f);
+    }
+  }
+  return FSA_OK;
+}

@@ -1,0 +1,248 @@
+/*
+ * fsa.h -- C ABI of libfsa: frame-block-sparse softmax attention for video
+ * diffusion transformers on AMD Instinct MI355X (gfx950).
+ *
+ * Each query frame t of each head attends only to a set A(t) of key/value
+ * frames.  The library builds those sets, picks frames by pooled scores,
+ * computes the attention with its log-sum-exp (LSE), and merges partial
+ * results over disjoint frame sets.
+ *
+ * Common conventions
+ * ------------------
+ *  - Every function returns fsa_status; FSA_OK is 0.  On any other status,
+ *    fsa_last_error() returns a message for the calling thread.
+ *  - Tensors are dense, contiguous, row-major.  q is [B][H][Nq][D]; k and v
+ *    are [B][H][Nk][D].  Token n of frame f is n = f*P + p (frame-major, P
+ *    tokens per frame), so Nq = Tq*P and Nk = Tk*P.
+ *  - Frame sets are idx [B][H][Tq][cap] int32 plus cnt [B][H][Tq] int32:
+ *    A(t) = idx[b][h][t][0 .. cnt-1], sorted ascending, no duplicates, every
+ *    entry in [0, Tk).  Entries past cnt are -1 when the library writes them
+ *    and ignored when it reads them.
+ *  - The caller owns every buffer.  The library never allocates or frees
+ *    device or host memory; scratch space comes in through explicit workspace
+ *    arguments.  It keeps no state beyond the thread-local error text.
+ *  - "device" functions only validate their host arguments, enqueue kernels
+ *    on `stream` (a hipStream_t; NULL = the default stream) and return; the
+ *    results are ready when the stream reaches that point.  Launch failures
+ *    return FSA_E_HIP.  "host" functions are synchronous and touch host
+ *    memory only; they need no GPU.
+ *  - Device kernels never read or write outside the buffers described here,
+ *    even for malformed frame lists: list entries outside [0, Tk) are
+ *    skipped and cnt is clamped to [0, cap].  Unsorted or duplicated lists
+ *    give unspecified (but memory-safe) results; fsa_validate_frame_sets
+ *    checks a host copy.
+ *
+ * Sources.  The operations follow these pages (gist.science technical
+ * summaries):
+ *  [LVSA]   LVSA, training-free sparse attention for long video diffusion:
+ *           §2 core mechanism (A(t) = G ∪ W(t), rotating anchors, widened
+ *           window, budget C) and its complexity paragraph.
+ *  [LF]     Light Forcing: §2.2 hierarchical sparse attention (mean-pooled
+ *           queries/keys, frame selection per query block, attention over
+ *           the selected frames only).
+ *  [ISPA]   ISPA, instance-specific parametric absorption: §2 item 1
+ *           dual-stream warmup and decomposable attention merged through LSE;
+ *           §3 item 2.
+ *  [HF]     Head Forcing: methodology §2, per-head KV sets (local, anchor,
+ *           memory with fast memory of recent frames).
+ *  [ARL2]   ARL2: §2.1 item 1, bidirectional softmax inside each frame
+ *           (the special case A(t) = {t}).
+ */
+#ifndef FSA_H_
+#define FSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSA_ABI_VERSION 1
+
+/* Largest number of heads one policy array may describe. */
+#define FSA_MAX_HEADS 64
+/* Largest frame-set capacity (entries per list) the kernels accept. */
+#define FSA_MAX_CAP 1024
+
+typedef enum fsa_status {
+  FSA_OK = 0,
+  FSA_E_ARG = 1,      /* null pointer, negative size, bad scalar argument      */
+  FSA_E_SHAPE = 2,    /* sizes inconsistent (N not a multiple of P, D, ...)    */
+  FSA_E_DTYPE = 3,    /* unsupported dtype / head_dim combination              */
+  FSA_E_CAPACITY = 4, /* cap or workspace too small for what is asked          */
+  FSA_E_LIST = 5,     /* a frame list is unsorted, duplicated or out of range  */
+  FSA_E_HIP = 6       /* the HIP runtime reported an error                     */
+} fsa_status;
+
+typedef enum fsa_dtype {
+  FSA_F32 = 0,  /* float32 inputs; computed in float32 end to end             */
+  FSA_BF16 = 1  /* bfloat16 inputs; MFMA with float32 accumulation            */
+} fsa_dtype;
+
+/* Frame-set policy of one head (fields a policy does not use are ignored). */
+typedef enum fsa_policy_kind {
+  FSA_POL_FULL = 0,        /* every KV frame: dense attention                   */
+  FSA_POL_LVSA = 1,        /* [LVSA] anchors G_s ∪ window widened to budget     */
+  FSA_POL_SINK_WINDOW = 2, /* [HF] local / anchor heads, [ISPA] local stream    */
+  FSA_POL_MEMORY = 3,      /* [HF] memory heads: selected frames ∪ recent       */
+  FSA_POL_RANGE = 4        /* frames lo..hi (e.g. [ISPA] history branch)        */
+} fsa_policy_kind;
+
+typedef struct fsa_head_policy {
+  int32_t kind;      /* fsa_policy_kind                                          */
+  int32_t n_sink;    /* SINK_WINDOW: frames 0..n_sink-1 are always kept          */
+  int32_t window;    /* LVSA: base window W; SINK_WINDOW: frames ending at e     */
+  int32_t budget;    /* LVSA: target |A(t)| = C                                  */
+  int32_t t_per;     /* LVSA: anchor period T_per (>= 1)                         */
+  int32_t step;      /* LVSA: denoising step s (anchors f with f%T_per == s%T_per)*/
+  int32_t topk;      /* MEMORY: selected frames per query group                  */
+  int32_t n_recent;  /* MEMORY: recent frames e-n_recent+1..e (fast memory)      */
+  int32_t lo, hi;    /* RANGE: inclusive frame range                             */
+} fsa_head_policy;
+
+/* ABI version the library was built with (FSA_ABI_VERSION). */
+int32_t fsa_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the next library call on this thread. */
+const char *fsa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Frame sets  [LVSA §2 core mechanism; HF methodology §2; ISPA §2 item 1]
+ *
+ * Query frame tq sits at KV frame offset+tq.  In chunked (autoregressive)
+ * mode `chunk` consecutive query frames form one chunk; the chunk's last KV
+ * frame is e = offset + (tq/chunk + 1)*chunk - 1, and all its frames share one
+ * set.  Per policy:
+ *   FULL         A = {0 .. Tk-1}.
+ *   LVSA         with T = Tk, t = offset+tq, r = step mod t_per:
+ *                G = {f : f mod t_per == r}; frames ordered by (|f-t|, f);
+ *                take the first k = min(window, T) of them and keep adding the
+ *                next one while |G ∪ first-k| < min(budget, T); A = G ∪ first-k.
+ *                (The window never shrinks below W and anchors are never
+ *                dropped, so A may exceed the budget when G ∪ W already does.)
+ *   SINK_WINDOW  A = {0..n_sink-1} ∪ {max(0, e-window+1) .. e}.
+ *   MEMORY       A = (topk selected frames of tq's group) ∪ {e-n_recent+1..e}.
+ *   RANGE        A = {max(0,lo) .. min(hi, Tk-1)}.
+ * ---------------------------------------------------------------------- */
+
+/* host.  Smallest cap that holds every set the policies can produce
+ * (an upper bound for LVSA/MEMORY, exact for the others). */
+fsa_status fsa_frame_set_capacity(int32_t H, const fsa_head_policy *policies /* host [H] */,
+                                  int32_t Tq, int32_t Tk, int32_t offset, int32_t chunk,
+                                  int32_t *cap_out /* host, 1 */);
+
+/* device.  Build idx/cnt for every (b, h, tq).
+ *   policies   host [H] (copied into the launch; H <= FSA_MAX_HEADS)
+ *   selected   device [B][H][Tq/chunk][topk_k] int32, the frames picked for
+ *              each query group (read for MEMORY heads only; may be NULL if no
+ *              head is MEMORY); entries outside [0,Tk) are skipped
+ *   idx        device [B][H][Tq][cap] int32 out (padded with -1)
+ *   cnt        device [B][H][Tq] int32 out
+ * Errors: FSA_E_ARG (bad sizes, Tq % chunk != 0, unknown kind, t_per < 1,
+ * budget/window < 0, MEMORY head without `selected`), FSA_E_CAPACITY (cap
+ * below fsa_frame_set_capacity or above FSA_MAX_CAP), FSA_E_HIP. */
+fsa_status fsa_build_frame_sets(int32_t B, int32_t H, int32_t Tq, int32_t Tk, int32_t offset,
+                                int32_t chunk, const fsa_head_policy *policies,
+                                const int32_t *selected, int32_t topk_k, int32_t cap,
+                                int32_t *idx, int32_t *cnt, void *stream);
+
+/* host.  The same construction on host buffers (selected, idx, cnt are host
+ * pointers).  Provided for callers that build lists on the CPU; the device
+ * path above does not use it. */
+fsa_status fsa_build_frame_sets_host(int32_t B, int32_t H, int32_t Tq, int32_t Tk,
+                                     int32_t offset, int32_t chunk,
+                                     const fsa_head_policy *policies, const int32_t *selected,
+                                     int32_t topk_k, int32_t cap, int32_t *idx, int32_t *cnt);
+
+/* host.  FSA_OK iff every list of a host copy of idx/cnt is sorted, unique,
+ * within [0, Tk) and 0 <= cnt <= cap; else FSA_E_LIST naming the first bad
+ * (b, h, t). */
+fsa_status fsa_validate_frame_sets(int32_t B, int32_t H, int32_t Tq, int32_t Tk, int32_t cap,
+                                   const int32_t *idx, const int32_t *cnt);
+
+/* ------------------------------------------------------------------------
+ * Frame selection  [LF §2.2 token compression + frame selection; HF §2
+ * memory heads]
+ *
+ * For each batch b, head h in [h_begin, h_end) and query group g (query
+ * frames g*q_group .. g*q_group+q_group-1):
+ *   qsum[d]   = sum of q over the group's tokens, float64, added one token at
+ *               a time in ascending token order;
+ *   ksum[f,d] = sum of k over frame f's P tokens, float64, ascending p;
+ *   score[f]  = sum over d of (qsum[d]*ksum[f,d]), each product rounded to
+ *               float64 then added in ascending d (no fused multiply-add);
+ * for candidate frames f in [cand_begin, cand_end).  Frames are ranked by
+ * (score descending, f ascending) and the first topk_k are written in
+ * ascending order.  Sums stand in for means (same ranking, no division).
+ * Every operation has a fixed order, so the result is bit-reproducible.
+ *   q, k        device, dtype dt, [B][H][Nq][D] and [B][H][Nk][D]
+ *   out_frames  device [B][H][Nq/(q_group*P)][topk_k] int32 (heads outside
+ *               [h_begin,h_end) untouched)
+ *   out_scores  device [B][H][G][cand_end-cand_begin] float64, or NULL
+ *   workspace   device, >= fsa_select_topk_workspace_size() bytes
+ * Errors: FSA_E_ARG (topk_k < 1 or > 64, topk_k > number of candidates,
+ * candidates outside [0, Tk), q_group does not divide Tq, bad head range),
+ * FSA_E_SHAPE, FSA_E_DTYPE, FSA_E_CAPACITY (workspace), FSA_E_HIP.
+ * Non-finite inputs give unspecified frames (a precondition). */
+fsa_status fsa_select_topk_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t D,
+                                          int32_t P, int32_t q_group, int32_t cand_begin,
+                                          int32_t cand_end, size_t *bytes);
+fsa_status fsa_select_topk_frames(const void *q, const void *k, int32_t dt, int32_t B,
+                                  int32_t H, int32_t Nq, int32_t Nk, int32_t D, int32_t P,
+                                  int32_t h_begin, int32_t h_end, int32_t q_group,
+                                  int32_t cand_begin, int32_t cand_end, int32_t topk_k,
+                                  int32_t *out_frames, double *out_scores, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse frame attention  [LVSA §2 core mechanism and complexity; LF §2.2
+ * execution over the selected frames; ISPA §2 item 1 (LSE output)]
+ *
+ * For every (b, h) and query token i of frame t = i / P:
+ *   S_ij  = scale * q_i . k_j   for keys j with j/P in A(t)
+ *   LSE_i = ln sum_j exp(S_ij)  (natural log)
+ *   O_i   = sum_j exp(S_ij - LSE_i) v_j
+ * An empty A(t) gives O_i = 0 and LSE_i = -inf.
+ *   scale      <= 0 selects 1/sqrt(D)
+ *   o          device [B][H][Nq][D] float32 out
+ *   lse        device [B][H][Nq] float32 out
+ *   workspace  device, >= fsa_sparse_frame_attn_workspace_size() bytes
+ *              (bf16: a float16, key-chunked transposed copy of v)
+ * Precision: dt = FSA_F32 computes in float32 throughout.  dt = FSA_BF16
+ * forms Q.K^T with bf16 MFMA (float32 accumulation), keeps the softmax and
+ * its row sums in float32, and forms P.V with float16 MFMA on float16
+ * probabilities and float16 values (float32 accumulation); O and LSE are
+ * float32.
+ * Supported: D in {64, 128}; P >= 1; Nq % P == 0; Nk % P == 0.
+ * Errors: FSA_E_ARG, FSA_E_SHAPE, FSA_E_DTYPE, FSA_E_CAPACITY, FSA_E_HIP. */
+fsa_status fsa_sparse_frame_attn_workspace_size(int32_t dt, int32_t B, int32_t H, int32_t Nk,
+                                                int32_t D, size_t *bytes);
+fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const void *v, int32_t dt,
+                                 int32_t B, int32_t H, int32_t Nq, int32_t Nk, int32_t D,
+                                 int32_t P, const int32_t *idx, const int32_t *cnt, int32_t cap,
+                                 float scale, float *o, float *lse, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * LSE merge  [ISPA §2 item 1, §3 item 2]
+ *
+ * For each of `rows` rows, with partials (o1, lse1) and (o2, lse2) over
+ * disjoint key sets:
+ *   M = max(lse1, lse2);  L = M + ln(exp(lse1-M) + exp(lse2-M));
+ *   O = exp(lse1-L)*o1 + exp(lse2-L)*o2.
+ * A partial with LSE = -inf contributes nothing; both -inf gives O = 0,
+ * L = -inf.  Exact only for disjoint key sets (the caller's duty).
+ *   o1, o2, o   device [rows][D] float32;  lse1, lse2, lse  device [rows]
+ *   o may alias o1 or o2 and lse may alias lse1 or lse2 (in-place merge).
+ * Errors: FSA_E_ARG (null pointer, rows < 0, D < 1), FSA_E_HIP. */
+fsa_status fsa_merge_lse(const float *o1, const float *lse1, const float *o2,
+                         const float *lse2, int64_t rows, int32_t D, float *o, float *lse,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSA_H_ */

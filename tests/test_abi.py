@@ -1,0 +1,140 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and every host-side argument check returns the documented status
+and message before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import frame_sparse_attention_amd as fsa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fsa.h")
+lib = fsa._lib
+
+BAD = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) == 11, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(fsa.EXPORTED)
+
+
+def test_abi_version_and_error_text():
+    assert fsa.abi_version() == 1
+    st = lib.fsa_merge_lse(BAD, BAD, BAD, BAD, -1, 4, BAD, BAD, None)
+    assert st == 1 and "rows" in fsa.last_error()
+    # a later successful call clears the text
+    assert lib.fsa_merge_lse(BAD, BAD, BAD, BAD, 0, 4, BAD, BAD, None) == 0
+    assert fsa.last_error() == ""
+
+
+def _attn(**kw):
+    a = dict(q=BAD, k=BAD, v=BAD, dt=1, B=1, H=2, Nq=64, Nk=64, D=128, P=16, idx=BAD, cnt=BAD,
+             cap=4, scale=0.0, o=BAD, lse=BAD, ws=BAD, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.fsa_sparse_frame_attn(a["q"], a["k"], a["v"], a["dt"], a["B"], a["H"], a["Nq"],
+                                     a["Nk"], a["D"], a["P"], a["idx"], a["cnt"], a["cap"],
+                                     a["scale"], a["o"], a["lse"], a["ws"], a["ws_bytes"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(dt=7), 3, "dtype"),
+    (dict(D=96), 3, "head_dim"),
+    (dict(B=-1), 1, "negative"),
+    (dict(P=0), 2, "P=0"),
+    (dict(Nq=60), 2, "Nq=60"),
+    (dict(Nk=70), 2, "Nk=70"),
+    (dict(cap=0), 4, "cap=0"),
+    (dict(cap=5000), 4, "cap=5000"),
+    (dict(q=None), 1, "null"),
+    (dict(k=None), 1, "k or v"),
+    (dict(ws_bytes=10), 4, "workspace"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(scale=float("inf")), 1, "scale"),
+])
+def test_attention_argument_errors(kw, status, text):
+    assert _attn(**kw) == status
+    assert text in fsa.last_error()
+
+
+def test_attention_empty_problem_is_ok_without_gpu():
+    assert _attn(Nq=0) == 0
+    assert _attn(B=0) == 0
+
+
+def test_workspace_size_queries():
+    n = ctypes.c_size_t()
+    assert lib.fsa_sparse_frame_attn_workspace_size(1, 1, 12, 65520, 128, ctypes.byref(n)) == 0
+    assert n.value == 12 * (65520 // 8) * 128 * 8 * 2
+    assert lib.fsa_sparse_frame_attn_workspace_size(1, 1, 1, 13, 64, ctypes.byref(n)) == 0
+    assert n.value == 2 * 64 * 8 * 2          # Nk rounded up to whole 8-key chunks
+    assert lib.fsa_sparse_frame_attn_workspace_size(0, 1, 1, 13, 64, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.fsa_sparse_frame_attn_workspace_size(0, 1, 1, 13, 80, ctypes.byref(n)) == 3
+    assert lib.fsa_select_topk_workspace_size(1, 12, 4680, 128, 1560, 3, 0, 57,
+                                              ctypes.byref(n)) == 0
+    assert n.value == 1 * 12 * (1 + 57) * 128 * 8
+
+
+def _topk(**kw):
+    a = dict(q=BAD, kp=BAD, dt=1, B=1, H=12, Nq=4680, Nk=93600, D=128, P=1560, h0=8, h1=12, qg=3,
+             c0=0, c1=57, k=8, out=BAD, scores=None, ws=BAD, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.fsa_select_topk_frames(a["q"], a["kp"], a["dt"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                      a["D"], a["P"], a["h0"], a["h1"], a["qg"], a["c0"], a["c1"],
+                                      a["k"], a["out"], a["scores"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(k=9, c1=8), 1, "exceeds"),
+    (dict(k=0), 1, "topk=0"),
+    (dict(k=65, c1=60), 1, "topk=65"),
+    (dict(c1=61), 1, "exceed Tk"),
+    (dict(c0=5, c1=5), 1, "empty"),
+    (dict(h0=10, h1=13), 1, "head range"),
+    (dict(qg=2), 2, "q_group"),
+    (dict(dt=5), 3, "dtype"),
+    (dict(ws_bytes=8), 4, "workspace"),
+    (dict(out=None), 1, "null"),
+])
+def test_topk_argument_errors(kw, status, text):
+    assert _topk(**kw) == status
+    assert text in fsa.last_error()
+
+
+def test_merge_argument_errors():
+    assert lib.fsa_merge_lse(BAD, BAD, BAD, BAD, 5, 0, BAD, BAD, None) == 1
+    assert "D=0" in fsa.last_error()
+    assert lib.fsa_merge_lse(None, BAD, BAD, BAD, 5, 4, BAD, BAD, None) == 1
+    assert "null" in fsa.last_error()
+
+
+def test_build_frame_sets_argument_errors():
+    pol = [dict(kind=fsa.LVSA, window=7, budget=21, t_per=6)]
+    with pytest.raises(fsa.FsaError, match="cap"):
+        fsa.build_frame_sets_host(pol, 1, 42, 42, cap=20)
+    with pytest.raises(fsa.FsaError, match="t_per"):
+        fsa.build_frame_sets_host([dict(kind=fsa.LVSA, window=7, budget=21, t_per=0)], 1, 4, 4)
+    with pytest.raises(fsa.FsaError, match="chunk"):
+        fsa.build_frame_sets_host([dict(kind=fsa.FULL)], 1, 4, 4, chunk=3)
+    with pytest.raises(fsa.FsaError, match="MEMORY"):
+        fsa.build_frame_sets_host([dict(kind=fsa.MEMORY, topk=2, n_recent=1)], 1, 3, 10,
+                                  offset=7, chunk=3)
+    with pytest.raises(fsa.FsaError, match="kind"):
+        fsa.build_frame_sets_host([dict(kind=9)], 1, 4, 4)
+    with pytest.raises(fsa.FsaError, match="exceed"):
+        fsa.build_frame_sets_host([dict(kind=fsa.SINK_WINDOW, window=2)], 1, 4, 4, offset=1)
+    with pytest.raises(fsa.FsaError, match="H=65"):
+        fsa.build_frame_sets_host([dict(kind=fsa.FULL)] * 65, 1, 4, 4)
