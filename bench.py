@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark: frame-sparse attention of one LVSA denoising step on one MI355X.
+
+A step is one pass of the whole hot path over the 42-frame LVSA workload
+(H=12, D=128, 42 latent frames x 1560 tokens, bf16 inputs with 4 outlier
+channels x8; budget C=21, window W=7, anchors every T_per=6 frames):
+  1. build the frame sets A_s(t) of step s on the device,
+  2. convert V to the float16 key-chunked layout the kernel reads,
+  3. sparse frame attention -> O (fp32) and LSE.
+Steps rotate s = 0..5 as the denoising loop does.  Inputs are resident in HBM
+before the timed region.  Printed: one JSON line with the whole-step effective
+TFLOP/s over attended pairs (4*D flop per attended (query, key) pair), the
+attention kernel's roofline position (HIP events on its launch stream), and
+the oracle timed on the host cores on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+METRIC = "effective attention TFLOP/s (attended pairs) + % of bf16 MFMA peak, 1 GPU"
+KERNEL_SOURCES = ["frame_sparse_attention_amd/csrc/attn_bf16.hip",
+                  "frame_sparse_attention_amd/csrc/attn_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_lvsa_T42_P1560_H12.traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(launch_units: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float):
+    """The oracle on whole query frames of step 0 until `budget_s` seconds pass."""
+    import numpy as np
+
+    from oracle import attention as oatt
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    order = [(int(h), int(t)) for h, t in zip(rng.integers(0, w.H, 10_000),
+                                               rng.integers(0, w.Tq, 10_000))]
+    done_pairs = 0
+    frames = 0
+    t0 = time.perf_counter()
+    kh_cache = {}
+    while frames < 2 or time.perf_counter() - t0 < budget_s:
+        h, t = order[frames]
+        if h not in kh_cache:
+            kh_cache.clear()
+            kh_cache[h] = (k[0, h].float().numpy(), v[0, h].float().numpy())
+        kk, vv = kh_cache[h]
+        qh = q[0, h, t * w.P:(t + 1) * w.P].float().numpy()
+        lst = idx[0, h, t, :cnt[0, h, t]]
+        mask = oatt.token_mask(lst, w.Tk, w.P)
+        oatt.attend_rows(qh, kk, vv, mask, 1.0 / np.sqrt(w.D))
+        done_pairs += w.P * int(mask.sum())
+        frames += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(4 * w.D * done_pairs / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{frames} whole query frames (head, frame) of step 0, "
+                      f"{w.P} rows x {int(cnt[0, 0, 0]) * w.P} keys each, float64 numpy, "
+                      f"{dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the oracle CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported; this build "
+              "has no multi-GPU path (the sharding design is described in DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import frame_sparse_attention_amd as fsa
+    import workloads as wl
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = wl.lvsa_shaped()
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = wl.make_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    cap = fsa.frame_set_capacity(w.policies, w.Tq, w.Tk)
+    idx = torch.empty((w.B, w.H, w.Tq, cap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((w.B, w.H, w.Tq), dtype=torch.int32, device=dev)
+    o = torch.empty((w.B, w.H, w.Nq, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    prep = torch.empty(fsa.sparse_frame_attn_workspace_size(fsa.BF16, w.B, w.H, w.Nk, w.D),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    policies = [w.with_step(s).policies for s in range(w.steps)]
+
+    # attended pairs per step (identical for every s: |A_s(t)| = C for all t)
+    pairs = []
+    for s in range(w.steps):
+        _, c = fsa.build_frame_sets(policies[s], w.B, w.Tq, w.Tk, cap=cap, device=dev)
+        pairs.append(int(c.to(torch.int64).sum().item()) * w.P * w.P)
+    flop_per_step = 4 * w.D * pairs[0]
+    assert all(p == pairs[0] for p in pairs)
+
+    def run_step(i, ev=None):
+        s = i % w.steps
+        if ev:
+            ev[0].record(stream)
+        fsa._check(fsa._lib.fsa_build_frame_sets(
+            w.B, w.H, w.Tq, w.Tk, 0, 1, fsa._policies(policies[s]), None, 0, cap,
+            idx.data_ptr(), cnt.data_ptr(), stream.cuda_stream))
+        if ev:
+            ev[1].record(stream)
+        fsa.prepare_values(vd, out=prep)
+        if ev:
+            ev[2].record(stream)
+        fsa.sparse_frame_attn_prepared(qd, kd, prep, idx, cnt, w.P, out=o, out_lse=lse)
+        if ev:
+            ev[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, no events (whole-step throughput)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-kernel durations with HIP events on the launch stream, same K steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        run_step(i, evs[i])
+    torch.cuda.synchronize()
+    build_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    prep_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    value = flop_per_step / (ms_per_step * 1e-3) / 1e12
+    achieved = flop_per_step / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic(1)
+    qtiles = -(-w.P // 128)
+    issued_pairs = w.B * w.H * w.Tq * qtiles * 128 * int(cnt[0, 0, 0].item()) * w.P
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), 4 outlier channels x8, bf16)",
+        "config": {"workload": w.name, "B": w.B, "heads": w.H, "head_dim": w.D,
+                   "frames": w.Tq, "tokens_per_frame": w.P, "budget_C": 21, "window_W": 7,
+                   "T_per": 6, "denoise_steps_rotated": w.steps,
+                   "attended_pairs_per_step": pairs[0], "flop_per_step": flop_per_step},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {"build_frame_sets": round(build_ms, 4),
+                       "prepare_values": round(prep_ms, 4),
+                       "sparse_frame_attn": round(attn_ms, 4)},
+        "issued_tile_tflops": round(4 * w.D * issued_pairs / (attn_ms * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] CPU baseline (oracle)", file=sys.stderr, flush=True)
+        # the baseline uses the frame sets of step 0
+        run_step(0)
+        torch.cuda.synchronize()
+        idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, idx_h, cnt_h, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

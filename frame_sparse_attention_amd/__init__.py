@@ -9,7 +9,8 @@ libfsa.so has not been built (python -m frame_sparse_attention_amd.build).
 
 Functions (same names as the C entry points, without the fsa_ prefix):
   frame_set_capacity, build_frame_sets, build_frame_sets_host,
-  validate_frame_sets, select_topk_frames, sparse_frame_attn, merge_lse,
+  validate_frame_sets, select_topk_frames, sparse_frame_attn, prepare_values,
+  sparse_frame_attn_prepared, merge_lse,
   plus the workspace-size queries, abi_version and last_error.
 """
 
@@ -75,6 +76,9 @@ _SIGS = {
     "fsa_sparse_frame_attn_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _psz]),
     "fsa_sparse_frame_attn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "fsa_prepare_values": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "fsa_sparse_frame_attn_prepared": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, _vp, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
     "fsa_merge_lse": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -258,6 +262,40 @@ def sparse_frame_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: to
                                       _ptr(idx), _ptr(cnt), idx.shape[3],
                                       float(scale) if scale is not None else 0.0, _ptr(o),
                                       _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device)))
+    return o, lse
+
+
+def prepare_values(v: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 V [B,H,Nk,D] -> the float16 key-chunked transposed copy the attention
+    reads (a uint8 buffer of sparse_frame_attn_workspace_size bytes)."""
+    _need_contig(v)
+    B, H, Nk, D = v.shape
+    need = sparse_frame_attn_workspace_size(_dtype_code(v), B, H, Nk, D)
+    if out is None:
+        out = torch.empty(max(1, need), dtype=torch.uint8, device=v.device)
+    _check(_lib.fsa_prepare_values(_ptr(v), _dtype_code(v), B, H, Nk, D, _ptr(out),
+                                   out.numel() * out.element_size(), _stream(v.device)))
+    return out
+
+
+def sparse_frame_attn_prepared(q: torch.Tensor, k: torch.Tensor, prepared: torch.Tensor,
+                               idx: torch.Tensor, cnt: torch.Tensor, P: int,
+                               scale: float | None = None, out: torch.Tensor | None = None,
+                               out_lse: torch.Tensor | None = None):
+    """Attention reading values already converted by prepare_values."""
+    _need_contig(q, k, prepared, idx, cnt)
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share one dtype")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    o = out if out is not None else torch.empty((B, H, Nq, D), dtype=torch.float32,
+                                                device=q.device)
+    lse = out_lse if out_lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
+                                                          device=q.device)
+    _check(_lib.fsa_sparse_frame_attn_prepared(
+        _ptr(q), _ptr(k), _ptr(prepared), _dtype_code(q), B, H, Nq, Nk, D, P, _ptr(idx),
+        _ptr(cnt), idx.shape[3], float(scale) if scale is not None else 0.0, _ptr(o), _ptr(lse),
+        prepared.numel() * prepared.element_size(), _stream(q.device)))
     return o, lse
 
 

@@ -8,10 +8,12 @@ namespace fsa {
 fsa_status launch_attn_f32(const float *q, const float *k, const float *v, const int32_t *idx,
                            const int32_t *cnt, int cap, int B, int H, int Nq, int Nk, int D,
                            int P, float scale, float *o, float *lse, hipStream_t stream);
-fsa_status launch_attn_bf16(const void *q, const void *k, const void *v, const int32_t *idx,
-                            const int32_t *cnt, int cap, int B, int H, int Nq, int Nk, int D,
-                            int P, float scale, float *o, float *lse, void *workspace,
-                            hipStream_t stream);
+fsa_status launch_prepare_values_bf16(const void *v, int B, int H, int Nk, int D, void *prepared,
+                                      hipStream_t stream);
+fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *prepared,
+                                     const int32_t *idx, const int32_t *cnt, int cap, int B,
+                                     int H, int Nq, int Nk, int D, int P, float scale, float *o,
+                                     float *lse, hipStream_t stream);
 size_t attn_bf16_workspace(long long heads, int Nk, int D);
 }  // namespace fsa
 
@@ -38,13 +40,11 @@ extern "C" fsa_status fsa_sparse_frame_attn_workspace_size(int32_t dt, int32_t B
   return FSA_OK;
 }
 
-extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const void *v,
-                                            int32_t dt, int32_t B, int32_t H, int32_t Nq,
-                                            int32_t Nk, int32_t D, int32_t P, const int32_t *idx,
-                                            const int32_t *cnt, int32_t cap, float scale,
-                                            float *o, float *lse, void *workspace,
-                                            size_t workspace_bytes, void *stream) {
-  fsa::clear_error();
+// Checks shared by the attention entry points; returns FSA_OK with *skip set
+// when there is nothing to compute.
+fsa_status check_attn(const void *q, const void *k, int32_t dt, int32_t B, int32_t H, int32_t Nq,
+                      int32_t Nk, int32_t D, int32_t P, const int32_t *idx, const int32_t *cnt,
+                      int32_t cap, float scale, const float *o, const float *lse, bool *skip) {
   fsa_status st = check_common(dt, B, H, Nk, D);
   if (st != FSA_OK) return st;
   FSA_REQUIRE(Nq >= 0, FSA_E_ARG, "Nq=%d must be >= 0", Nq);
@@ -54,9 +54,57 @@ extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const 
   FSA_REQUIRE(cap >= 1 && cap <= FSA_MAX_CAP, FSA_E_CAPACITY, "cap=%d outside [1, %d]", cap,
               FSA_MAX_CAP);
   FSA_REQUIRE(std::isfinite(scale), FSA_E_ARG, "scale is not finite");
-  if ((long long)B * H * Nq == 0) return FSA_OK;
+  *skip = (long long)B * H * Nq == 0;
+  if (*skip) return FSA_OK;
   FSA_REQUIRE(q && o && lse && idx && cnt, FSA_E_ARG, "null pointer argument");
-  FSA_REQUIRE(Nk == 0 || (k && v), FSA_E_ARG, "k or v is NULL");
+  FSA_REQUIRE(Nk == 0 || k, FSA_E_ARG, "k or v is NULL");
+  return FSA_OK;
+}
+
+extern "C" fsa_status fsa_prepare_values(const void *v, int32_t dt, int32_t B, int32_t H,
+                                         int32_t Nk, int32_t D, void *prepared,
+                                         size_t prepared_bytes, void *stream) {
+  fsa::clear_error();
+  fsa_status st = check_common(dt, B, H, Nk, D);
+  if (st != FSA_OK) return st;
+  FSA_REQUIRE(dt == FSA_BF16, FSA_E_DTYPE, "prepared values exist for bf16 only");
+  const size_t need = fsa::attn_bf16_workspace((long long)B * H, Nk, D);
+  if (need == 0) return FSA_OK;
+  FSA_REQUIRE(v && prepared, FSA_E_ARG, "null pointer argument");
+  FSA_REQUIRE(prepared_bytes >= need, FSA_E_CAPACITY, "prepared buffer of %zu bytes < %zu needed",
+              prepared_bytes, need);
+  return fsa::launch_prepare_values_bf16(v, B, H, Nk, D, prepared, fsa::as_stream(stream));
+}
+
+extern "C" fsa_status fsa_sparse_frame_attn_prepared(
+    const void *q, const void *k, const void *prepared, int32_t dt, int32_t B, int32_t H,
+    int32_t Nq, int32_t Nk, int32_t D, int32_t P, const int32_t *idx, const int32_t *cnt,
+    int32_t cap, float scale, float *o, float *lse, size_t prepared_bytes, void *stream) {
+  fsa::clear_error();
+  bool skip = false;
+  fsa_status st = check_attn(q, k, dt, B, H, Nq, Nk, D, P, idx, cnt, cap, scale, o, lse, &skip);
+  if (st != FSA_OK || skip) return st;
+  FSA_REQUIRE(dt == FSA_BF16, FSA_E_DTYPE, "prepared values exist for bf16 only");
+  const size_t need = fsa::attn_bf16_workspace((long long)B * H, Nk, D);
+  FSA_REQUIRE(need == 0 || prepared, FSA_E_ARG, "k or v is NULL");
+  FSA_REQUIRE(prepared_bytes >= need, FSA_E_CAPACITY, "prepared buffer of %zu bytes < %zu needed",
+              prepared_bytes, need);
+  if (scale <= 0.f) scale = 1.f / std::sqrt((float)D);
+  return fsa::launch_attn_bf16_prepared(q, k, prepared, idx, cnt, cap, B, H, Nq, Nk, D, P, scale,
+                                        o, lse, fsa::as_stream(stream));
+}
+
+extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const void *v,
+                                            int32_t dt, int32_t B, int32_t H, int32_t Nq,
+                                            int32_t Nk, int32_t D, int32_t P, const int32_t *idx,
+                                            const int32_t *cnt, int32_t cap, float scale,
+                                            float *o, float *lse, void *workspace,
+                                            size_t workspace_bytes, void *stream) {
+  fsa::clear_error();
+  bool skip = false;
+  fsa_status st = check_attn(q, k, dt, B, H, Nq, Nk, D, P, idx, cnt, cap, scale, o, lse, &skip);
+  if (st != FSA_OK || skip) return st;
+  FSA_REQUIRE(Nk == 0 || v, FSA_E_ARG, "k or v is NULL");
   if (scale <= 0.f) scale = 1.f / std::sqrt((float)D);
   hipStream_t s = fsa::as_stream(stream);
   if (dt == FSA_F32)
@@ -67,6 +115,10 @@ extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const 
   FSA_REQUIRE(need == 0 || workspace != nullptr, FSA_E_ARG, "workspace is NULL");
   FSA_REQUIRE(workspace_bytes >= need, FSA_E_CAPACITY, "workspace of %zu bytes < %zu needed",
               workspace_bytes, need);
-  return fsa::launch_attn_bf16(q, k, v, idx, cnt, cap, B, H, Nq, Nk, D, P, scale, o, lse,
-                               workspace, s);
+  if (need > 0) {
+    st = fsa::launch_prepare_values_bf16(v, B, H, Nk, D, workspace, s);
+    if (st != FSA_OK) return st;
+  }
+  return fsa::launch_attn_bf16_prepared(q, k, workspace, idx, cnt, cap, B, H, Nq, Nk, D, P,
+                                        scale, o, lse, s);
 }

@@ -307,20 +307,26 @@ size_t attn_bf16_workspace(long long heads, int Nk, int D) {
   return (size_t)heads * NkC * D * 8 * sizeof(_Float16);
 }
 
-fsa_status launch_attn_bf16(const void *q, const void *k, const void *v, const int32_t *idx,
-                            const int32_t *cnt, int cap, int B, int H, int Nq, int Nk, int D,
-                            int P, float scale, float *o, float *lse, void *workspace,
-                            hipStream_t stream) {
+fsa_status launch_prepare_values_bf16(const void *v, int B, int H, int Nk, int D, void *prepared,
+                                      hipStream_t stream) {
   const long long heads = (long long)B * H;
   const int NkC = (Nk + 7) / 8;
-  auto vt = static_cast<_Float16 *>(workspace);
-  if (NkC > 0) {
-    const long long total = heads * NkC * D;
-    const long long blocks = (total + 255) / 256;
-    FSA_REQUIRE(blocks < (1LL << 31), FSA_E_SHAPE, "V too large (%lld blocks)", blocks);
-    hipLaunchKernelGGL(v_to_f16_chunked_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t *>(v), vt, total, Nk, NkC, D);
-  }
+  if (NkC == 0 || heads == 0) return FSA_OK;
+  const long long total = heads * NkC * D;
+  const long long blocks = (total + 255) / 256;
+  FSA_REQUIRE(blocks < (1LL << 31), FSA_E_SHAPE, "V too large (%lld blocks)", blocks);
+  hipLaunchKernelGGL(v_to_f16_chunked_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t *>(v), static_cast<_Float16 *>(prepared), total,
+                     Nk, NkC, D);
+  return check_launch("prepare_values");
+}
+
+fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *prepared,
+                                     const int32_t *idx, const int32_t *cnt, int cap, int B,
+                                     int H, int Nq, int Nk, int D, int P, float scale, float *o,
+                                     float *lse, hipStream_t stream) {
+  const long long heads = (long long)B * H;
+  const int NkC = (Nk + 7) / 8;
   const int Tq = Nq / P;
   const int qtiles = (P + kRows - 1) / kRows;
   const long long blocks = heads * Tq * qtiles;
@@ -328,6 +334,7 @@ fsa_status launch_attn_bf16(const void *q, const void *k, const void *v, const i
   const float scale_log2 = scale * kLog2e;
   auto qq = static_cast<const uint16_t *>(q);
   auto kk = static_cast<const uint16_t *>(k);
+  auto vt = static_cast<const _Float16 *>(prepared);
   if (D == 64)
     hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        qq, kk, vt, idx, cnt, cap, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, o,

@@ -225,6 +225,28 @@ fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const void *v, in
                                  float scale, float *o, float *lse, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* device.  The two halves of fsa_sparse_frame_attn, for callers that reuse
+ * the same values across calls (an autoregressive KV cache attended by every
+ * denoising step and by several branches):
+ *   fsa_prepare_values           bf16 only: writes the float16, key-chunked
+ *                                transposed copy of v into `prepared`
+ *                                (>= fsa_sparse_frame_attn_workspace_size
+ *                                bytes, layout [B*H][ceil(Nk/8)][D][8]; keys
+ *                                past Nk are zero).
+ *   fsa_sparse_frame_attn_prepared  the attention itself, reading that copy
+ *                                instead of v.
+ * fsa_sparse_frame_attn(v, workspace) equals prepare(v -> workspace)
+ * followed by prepared(workspace).  Errors as above; FSA_E_DTYPE for
+ * dt != FSA_BF16. */
+fsa_status fsa_prepare_values(const void *v, int32_t dt, int32_t B, int32_t H, int32_t Nk,
+                              int32_t D, void *prepared, size_t prepared_bytes, void *stream);
+fsa_status fsa_sparse_frame_attn_prepared(const void *q, const void *k, const void *prepared,
+                                          int32_t dt, int32_t B, int32_t H, int32_t Nq,
+                                          int32_t Nk, int32_t D, int32_t P, const int32_t *idx,
+                                          const int32_t *cnt, int32_t cap, float scale,
+                                          float *o, float *lse, size_t prepared_bytes,
+                                          void *stream);
+
 /* ------------------------------------------------------------------------
  * LSE merge  [ISPA §2 item 1, §3 item 2]
  *

@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(fsa.EXPORTED)
@@ -72,6 +72,20 @@ def test_attention_argument_errors(kw, status, text):
 def test_attention_empty_problem_is_ok_without_gpu():
     assert _attn(Nq=0) == 0
     assert _attn(B=0) == 0
+
+
+def test_prepared_entry_points_argument_errors():
+    assert lib.fsa_prepare_values(BAD, 0, 1, 2, 64, 128, BAD, 1 << 40, None) == 3
+    assert "bf16 only" in fsa.last_error()
+    assert lib.fsa_prepare_values(BAD, 1, 1, 2, 64, 128, BAD, 100, None) == 4
+    assert "prepared buffer" in fsa.last_error()
+    assert lib.fsa_prepare_values(BAD, 1, 1, 2, 0, 128, None, 0, None) == 0
+    st = lib.fsa_sparse_frame_attn_prepared(BAD, BAD, BAD, 0, 1, 2, 64, 64, 128, 16, BAD, BAD, 4,
+                                            0.0, BAD, BAD, 1 << 40, None)
+    assert st == 3 and "bf16 only" in fsa.last_error()
+    st = lib.fsa_sparse_frame_attn_prepared(BAD, BAD, BAD, 1, 1, 2, 64, 64, 128, 16, BAD, BAD, 4,
+                                            0.0, BAD, BAD, 8, None)
+    assert st == 4 and "prepared buffer" in fsa.last_error()
 
 
 def test_workspace_size_queries():

@@ -1,0 +1,156 @@
+"""GPU parity of the sparse frame attention against the oracle, element by
+element, on sizes the oracle finishes in seconds: several query tiles and key
+tiles, ragged tails (P not a multiple of the 128-row / 64-key tiles or of the
+8-key chunks), D = 64 and 128, and the degenerate frame sets (empty, one
+frame, the own frame only, all frames, scattered lists, malformed entries)."""
+
+import numpy as np
+import pytest
+import torch
+
+import frame_sparse_attention_amd as fsa
+import workloads as wl
+from oracle import attention as oatt
+from oracle import frame_sets as ofs
+
+from _parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _rand(shape, dtype, seed, outliers=0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(*shape, generator=g)
+    if outliers:
+        ch = torch.randperm(shape[-1], generator=g)[:outliers]
+        x[..., ch] *= 8.0
+    return x.to(dtype).contiguous()
+
+
+def _lists_to_arrays(lists, B, H):
+    """lists[b][h][t] -> padded idx/cnt int32 tensors."""
+    Tq = len(lists[0][0])
+    cap = max(1, max(len(a) for lb in lists for lh in lb for a in lh))
+    idx = np.full((B, H, Tq, cap), -1, np.int32)
+    cnt = np.zeros((B, H, Tq), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for t, a in enumerate(lists[b][h]):
+                idx[b, h, t, :len(a)] = a
+                cnt[b, h, t] = len(a)
+    return torch.from_numpy(idx), torch.from_numpy(cnt)
+
+
+def _run_and_check(q, k, v, idx, cnt, P, kind, what, scale=None):
+    _say(what)
+    o, lse = fsa.sparse_frame_attn(q.to(DEV), k.to(DEV), v.to(DEV), idx.to(DEV), cnt.to(DEV),
+                                   P, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oatt.sparse_frame_attention(q.float().numpy(), k.float().numpy(),
+                                               v.float().numpy(), idx.numpy(), cnt.numpy(), P,
+                                               scale=scale)
+    return assert_close(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, kind, what)
+
+
+def test_tiny_f32_workload_in_full():
+    w = wl.tiny_f32()
+    q, k, v = wl.make_qkv(w)
+    idx, cnt = fsa.build_frame_sets(w.policies, w.B, w.Tq, w.Tk, device=DEV)
+    oidx, ocnt = ofs.build(w.policies, w.B, w.Tq, w.Tk, cap=idx.shape[3])
+    assert np.array_equal(idx.cpu().numpy(), oidx) and np.array_equal(cnt.cpu().numpy(), ocnt)
+    _run_and_check(q, k, v, idx.cpu(), cnt.cpu(), w.P, "f32", "tiny fp32 workload")
+
+
+@pytest.mark.parametrize("D,P", [(64, 13), (128, 16), (128, 70)])
+def test_f32_ragged_and_scattered(D, P):
+    B, H, T = 1, 2, 5
+    q, k, v = (_rand((B, H, T * P, D), torch.float32, s) for s in (1, 2, 3))
+    lists = [[[[0], [0, 2, 4], [], [1, 2, 3, 4], [3]], [[4], [0, 1], [2], [0, 1, 2, 3, 4], []]]]
+    idx, cnt = _lists_to_arrays(lists, B, H)
+    _run_and_check(q, k, v, idx, cnt, P, "f32", f"fp32 D={D} P={P}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("P", [1, 5, 8, 13, 64, 100, 130, 200])
+def test_bf16_shapes_and_lists(D, P):
+    B, H, T = 1, 2, 6
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s, outliers=4) for s in (4, 5, 6))
+    lists = [[[[0], [0, 1, 2, 3, 4, 5], [1, 3, 5], [3], [], [0, 2, 3, 4]],
+              [[5], [4, 5], [0, 5], [2, 3], [1], [0, 1, 2, 3, 4, 5]]]]
+    idx, cnt = _lists_to_arrays(lists, B, H)
+    _run_and_check(q, k, v, idx, cnt, P, "bf16", f"bf16 D={D} P={P}")
+
+
+@pytest.mark.parametrize("s", range(6))
+def test_bf16_lvsa_shrunk(s):
+    # LVSA policy of the 42-frame workload (C=21, W=7, T_per=6, outliers x8) on
+    # fewer heads and a ragged P=200: every step of the anchor rotation.
+    w = wl.lvsa_shaped(s).shrunk(H=2, P=200)
+    q, k, v = wl.make_qkv(w)
+    idx, cnt = fsa.build_frame_sets(w.policies[:2], w.B, w.Tq, w.Tk, device=DEV)
+    _run_and_check(q, k, v, idx.cpu(), cnt.cpu(), w.P, "bf16", f"lvsa T=42 P=200 step {s}")
+
+
+def test_bf16_own_frame_only_and_full():
+    # ARL2 §2.1 intra-frame branch: A(t) = {t}; and the FULL set (dense attention)
+    B, H, T, P, D = 1, 2, 4, 150, 128
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s) for s in (7, 8, 9))
+    own = [[[[t] for t in range(T)] for _ in range(H)]]
+    idx, cnt = _lists_to_arrays(own, B, H)
+    _run_and_check(q, k, v, idx, cnt, P, "bf16", "own frame only")
+    full = [[[list(range(T)) for _ in range(T)] for _ in range(H)]]
+    idx, cnt = _lists_to_arrays(full, B, H)
+    _run_and_check(q, k, v, idx, cnt, P, "bf16", "full set")
+
+
+def test_bf16_explicit_scale_and_batch():
+    B, H, T, P, D = 2, 3, 3, 40, 64
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s) for s in (10, 11, 12))
+    lists = [[[[0, 1], [2], [0, 2]] for _ in range(H)] for _ in range(B)]
+    lists[1][2] = [[1], [0, 1, 2], []]
+    idx, cnt = _lists_to_arrays(lists, B, H)
+    _run_and_check(q, k, v, idx, cnt, P, "bf16", "scale 0.05, batch 2", scale=0.05)
+
+
+def test_malformed_entries_are_skipped_not_read():
+    # entries outside [0, Tk) are skipped and cnt is clamped to cap: the result
+    # equals attention over the valid entries only
+    B, H, T, P, D = 1, 1, 3, 24, 128
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s) for s in (13, 14, 15))
+    idx = torch.tensor([[[[0, 99, 2], [-5, 1, 7], [2, 1000, -1]]]], dtype=torch.int32)
+    cnt = torch.tensor([[[3, 3, 9]]], dtype=torch.int32)
+    good = [[[[0, 2], [1], [2]]]]
+    gidx, gcnt = _lists_to_arrays(good, B, H)
+    _say("malformed entries")
+    o, lse = fsa.sparse_frame_attn(q.to(DEV), k.to(DEV), v.to(DEV), idx.to(DEV), cnt.to(DEV), P)
+    o2, lse2 = fsa.sparse_frame_attn(q.to(DEV), k.to(DEV), v.to(DEV), gidx.to(DEV),
+                                     gcnt.to(DEV), P)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_empty_sets_give_zero_and_minus_inf():
+    B, H, T, P, D = 1, 2, 2, 33, 128
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s) for s in (16, 17, 18))
+    idx = torch.full((B, H, T, 2), -1, dtype=torch.int32)
+    cnt = torch.zeros((B, H, T), dtype=torch.int32)
+    _say("empty sets")
+    o, lse = fsa.sparse_frame_attn(q.to(DEV), k.to(DEV), v.to(DEV), idx.to(DEV), cnt.to(DEV), P)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(lse == -float("inf"))
+
+
+def test_zero_queries_closed_form():
+    # Q = 0: every attended key has score 0, so O is the mean of the attended V
+    # rows and LSE = ln(|A|·P) exactly
+    B, H, T, P, D = 1, 1, 4, 96, 128
+    q = torch.zeros(B, H, T * P, D, dtype=torch.bfloat16)
+    k, v = (_rand((B, H, T * P, D), torch.bfloat16, s) for s in (19, 20))
+    lists = [[[[0], [0, 1], [1, 2, 3], [0, 1, 2, 3]]]]
+    idx, cnt = _lists_to_arrays(lists, B, H)
+    _run_and_check(q, k, v, idx, cnt, P, "bf16", "zero queries")

@@ -1,0 +1,112 @@
+"""GPU parity on the five synthetic workloads at their full sizes, in the same
+launch configuration the benchmark times: frame sets built on the device,
+attention over them, checked against the oracle on sampled query rows (rows at
+tile edges plus random ones); the AR-chunk and decomposable workloads in full."""
+
+import numpy as np
+import pytest
+import torch
+
+import frame_sparse_attention_amd as fsa
+import workloads as wl
+from oracle import frame_sets as ofs
+from oracle import merge as omerge
+from oracle import topk as otopk
+
+from _parity import assert_close, oracle_rows, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _attn(w, q, k, v, policies, selected=None):
+    idx, cnt = fsa.build_frame_sets(policies, w.B, w.Tq, w.Tk, w.offset, w.chunk, selected,
+                                    device=DEV)
+    o, lse = fsa.sparse_frame_attn(q, k, v, idx, cnt, w.P)
+    torch.cuda.synchronize()
+    return idx.cpu(), cnt.cpu(), o, lse
+
+
+def test_lvsa_42_frames_every_step():
+    w = wl.lvsa_shaped()
+    q, k, v = wl.make_qkv(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for s in range(w.steps):
+        ws = w.with_step(s)
+        _say(f"{w.name} step {s}")
+        idx, cnt, o, lse = _attn(ws, qd, kd, vd, ws.policies)
+        oidx, ocnt = ofs.build(ws.policies, ws.B, ws.Tq, ws.Tk, cap=idx.shape[3])
+        assert np.array_equal(idx.numpy(), oidx) and np.array_equal(cnt.numpy(), ocnt)
+        frames = sorted({0, 1, 20, 21, 40, 41} | set(np.random.default_rng(s).integers(0, 42, 4)))
+        rows = sample_rows(w.P, frames, 8, seed=s)
+        o_ref, l_ref = oracle_rows(q, k, v, idx, cnt, w.P, rows)
+        assert_close(o[:, :, rows].cpu().numpy(), lse[:, :, rows].cpu().numpy(), o_ref, l_ref,
+                     "bf16", f"{w.name} step {s} ({rows.size} rows x 12 heads)")
+
+
+def test_ar_chunk_per_head_policies_in_full():
+    w = wl.ar_chunk()
+    q, k, v = wl.make_qkv(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    _say(f"{w.name}: top-k + build + attention")
+    sel = fsa.select_topk_frames(qd, kd, w.P, 8, 12, 3, 0, 57, 8)
+    idx, cnt, o, lse = _attn(w, qd, kd, vd, w.policies, sel)
+    # oracle frame sets from the oracle's own top-k
+    sel_lists = [[[[]] for _ in range(12)]]
+    for h in range(8, 12):
+        f, _ = otopk.select_topk_frames(q[0, h].float().numpy(), k[0, h].float().numpy(), w.P,
+                                        np.arange(w.Nq), range(57), 8)
+        sel_lists[0][h] = [f]
+    oidx, ocnt = ofs.build(w.policies, w.B, w.Tq, w.Tk, w.offset, w.chunk, sel_lists,
+                           cap=idx.shape[3])
+    assert np.array_equal(idx.numpy(), oidx) and np.array_equal(cnt.numpy(), ocnt)
+    rows = np.arange(w.Nq)
+    o_ref, l_ref = oracle_rows(q, k, v, idx, cnt, w.P, rows)
+    assert_close(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16", f"{w.name} all rows")
+
+
+def test_decomposable_branches_merge_to_union():
+    w = wl.decomposable()
+    q, k, v = wl.make_qkv(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = {}
+    for name in ("A", "B", "U"):
+        _say(f"{w.name} branch {name}")
+        out[name] = _attn(w, qd, kd, vd, w.branches[name])
+    _say(f"{w.name} merge A+B")
+    om, lm = fsa.merge_lse(out["A"][2], out["A"][3], out["B"][2], out["B"][3])
+    torch.cuda.synchronize()
+    rows = sample_rows(w.P, range(w.Tq), 48, seed=4)
+    ref = {}
+    for name in ("A", "B", "U"):
+        idx, cnt, o, lse = out[name]
+        ref[name] = oracle_rows(q, k, v, idx, cnt, w.P, rows)
+        assert_close(o[:, :, rows].cpu().numpy(), lse[:, :, rows].cpu().numpy(), *ref[name],
+                     "bf16", f"{w.name} branch {name}")
+    # the merged partials equal single-pass attention over all 49 frames
+    assert_close(om[:, :, rows].cpu().numpy(), lm[:, :, rows].cpu().numpy(), *ref["U"], "bf16",
+                 f"{w.name} merge(A,B) vs oracle union")
+    mo, ml = omerge.merge_lse(*ref["A"], *ref["B"])
+    assert np.max(np.abs(mo - ref["U"][0])) < 1e-12
+    assert (om - out["U"][2]).abs().max().item() <= 1e-2
+
+
+@pytest.mark.parametrize("s", [0, 5])
+def test_long_video_sampled_rows(s):
+    w = wl.long_video(s)
+    _say(f"{w.name}: generating inputs")
+    q, k, v = wl.make_qkv(w)
+    _say(f"{w.name} step {s}")
+    idx, cnt, o, lse = _attn(w, q.to(DEV), k.to(DEV), v.to(DEV), w.policies)
+    oidx, ocnt = ofs.build(w.policies, w.B, w.Tq, w.Tk, cap=idx.shape[3])
+    assert np.array_equal(idx.numpy(), oidx) and np.array_equal(cnt.numpy(), ocnt)
+    frames = [0, 1, 62, 63, 124, 125]
+    rows = sample_rows(w.P, frames, 8, seed=s)
+    heads = [0, 7, 23] if s else list(range(0, 24, 4))
+    o_ref, l_ref = oracle_rows(q, k, v, idx, cnt, w.P, rows, heads=heads)
+    assert_close(o[:, heads][:, :, rows].cpu().numpy(), lse[:, heads][:, :, rows].cpu().numpy(),
+                 o_ref, l_ref, "bf16", f"{w.name} step {s} ({rows.size} rows x {len(heads)} heads)")
