@@ -45,9 +45,6 @@ constexpr int kWaitVm0 = 0x0F70;
 
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Value of x in the lane 32 apart (the other half of the wavefront).
-__device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
-
 // ---------------------------------------------------------------------------
 // V prepass: Vt[head][kc][d][e] = float16(V[head][8*kc + e][d]), zero past Nk.
 // One thread per (head, kc, d); each reads 8 rows (coalesced across d) and
@@ -76,15 +73,24 @@ __device__ inline int key_slot(int kk) {
   return (kk & ~12) | ((kk >> 1) & 4) | ((kk << 1) & 8);
 }
 
-struct Tile {
-  int r;             // run index
-  long long start;   // first key of the run
-  long long end;     // one past the last key of the run
-  long long n0;      // first key of the tile (multiple of 8, <= start on a run's first tile)
+// The reference max of a row moves exactly to the running max: the largest
+// probability of a row is then exactly 1.0, which float16 holds without error
+// (a stale reference would put it anywhere in [1, 2^k) and give it the full
+// float16 rounding error, which on peaked rows with large values approaches
+// the output tolerance).  Tiles where no row of the wavefront found a new max
+// skip the rescale altogether; that is bitwise identical to multiplying by 1.
+// Cross-half exchange: {x, x of lane l^32} via v_permlane32_swap.
+struct HalfPair {
+  float a, b;
 };
+__device__ inline HalfPair with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
 
 template <int D>
-__global__ void __launch_bounds__(kThreads) attn_bf16_kernel(
+__global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const _Float16 *__restrict__ vt, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ cnt, int cap, int H, int Nq, int Nk, int NkC, int P, int Tq,
@@ -101,7 +107,8 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(
   __shared__ int s_nruns;
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64, j = lane % 32, g = lane / 32;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, j = lane % 32, g = lane / 32;
 
   int tile = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int qt = tile % qtiles;
@@ -132,77 +139,91 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-  float m = -INFINITY;  // running row max, in scaled base-2 units
-  float l = 0.f;        // running row sum (this lane's half of the keys)
+  float m = -INFINITY;  // running row max, scaled base-2 units
+  float l = 0.f;        // running row sum against m (this lane's half of the keys)
 
   const uint16_t *kh = k + head * (long long)Nk * D;
   const _Float16 *vh = vt + head * (long long)NkC * D * 8;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // Tile loads go straight from HBM into LDS (global_load_lds_dwordx4): each
   // wavefront instruction fills 64 consecutive 16-byte LDS units, one per
   // lane, and the lane picks the global chunk that belongs at its unit.
   // K: unit u -> slot u / NCH, stored chunk u % NCH, which holds logical chunk
   // (u % NCH) ^ (slot & SWZ) of key key_slot(slot).  V^T: unit u is the u-th
-  // 16-byte chunk of the tile, contiguous in the workspace.
-  int koff[KLD];
+  // 16-byte chunk of the tile, contiguous in the workspace.  Per-lane offsets
+  // are fixed; only the tile's base pointer changes.
+  int koff[KLD], kkey[KLD];
 #pragma unroll
   for (int it = 0; it < KLD; ++it) {
-    const int u = (it * 4 + wave_u) * 64 + lane;
+    const int u = (it * 4 + wave) * 64 + lane;
     const int slot = u / NCH, pc = u % NCH;
-    const int kk = key_slot(slot), c = pc ^ (slot & SWZ);
-    koff[it] = kk * D + c * 8;
+    kkey[it] = key_slot(slot);
+    koff[it] = kkey[it] * D + (pc ^ (slot & SWZ)) * 8;
   }
-  auto issue_tile = [&](long long n0, int b) {
-    const bool k_tail = n0 + kTileKeys > Nk;
+  auto issue_tile = [&](int n0, int bsel) {
+    const uint16_t *kbase = kh + (long long)n0 * D;
+    if (n0 + kTileKeys <= Nk) {
 #pragma unroll
-    for (int it = 0; it < KLD; ++it) {
-      const uint16_t *src = kh + n0 * D + koff[it];
-      if (k_tail) {
-        long long key = n0 + koff[it] / D;
-        key = key < Nk ? key : Nk - 1;
-        src = kh + key * D + koff[it] % D;
+      for (int it = 0; it < KLD; ++it)
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(kbase + koff[it]),
+            (__attribute__((address_space(3))) void *)&s_k[bsel][(it * 4 + wave) * 1024], 16, 0,
+            0);
+    } else {
+      // last tile of the keys: rows past Nk repeat row Nk-1 (their scores are masked)
+#pragma unroll
+      for (int it = 0; it < KLD; ++it) {
+        const int over = n0 + kkey[it] - (Nk - 1);
+        const int off = over > 0 ? koff[it] - over * D : koff[it];
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(kbase + off),
+            (__attribute__((address_space(3))) void *)&s_k[bsel][(it * 4 + wave) * 1024], 16, 0,
+            0);
       }
-      __builtin_amdgcn_global_load_lds(
-          (const void *)src,
-          (__attribute__((address_space(3))) void *)&s_k[b][(it * 4 + wave_u) * 1024], 16, 0, 0);
     }
-    const bool v_tail = n0 / 8 + kTileKeys / 8 > NkC;
+    const int c0 = n0 / 8;
+    const _Float16 *vbase = vh + (long long)c0 * D * 8;
+    const bool v_whole = c0 + kTileKeys / 8 <= NkC;
 #pragma unroll
     for (int it = 0; it < VLD; ++it) {
-      const int u = (it * 4 + wave_u) * 64 + lane;
-      long long chunk = n0 / 8 + u / D;
-      if (v_tail) chunk = chunk < NkC ? chunk : NkC - 1;
-      const _Float16 *src = vh + (chunk * D + u % D) * 8;
+      const int u = (it * 4 + wave) * 64 + lane;
+      int off = u * 8;
+      if (!v_whole) {
+        const int over = c0 + u / D - (NkC - 1);
+        if (over > 0) off -= over * D * 8;
+      }
       __builtin_amdgcn_global_load_lds(
-          (const void *)src,
-          (__attribute__((address_space(3))) void *)&s_v[b][(it * 4 + wave_u) * 1024], 16, 0, 0);
+          (const void *)(vbase + off),
+          (__attribute__((address_space(3))) void *)&s_v[bsel][(it * 4 + wave) * 1024], 16, 0, 0);
     }
-  };
-  auto first_tile = [&](int r) {
-    Tile t;
-    t.r = r;
-    if (r < nruns) {
-      t.start = (long long)s_lo[r] * P;
-      t.end = (long long)(s_hi[r] + 1) * P;
-      t.n0 = t.start & ~7LL;
-    } else {
-      t.start = t.end = t.n0 = 0;
-    }
-    return t;
   };
 
-  Tile cur = first_tile(0);
-  if (nruns > 0) issue_tile(cur.n0, 0);
+  // tile cursor: run r, run key range [start, end), tile start n0 (multiple of 8)
+  int r = 0, start = 0, end = 0, n0 = 0;
+  if (nruns > 0) {
+    start = s_lo[0] * P;
+    end = (s_hi[0] + 1) * P;
+    n0 = start & ~7;
+    issue_tile(n0, 0);
+  }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
+
+  // per-lane key bounds are compared against compile-time key offsets
+  const int g8 = 8 * g;
   int buf = 0;
-  while (cur.r < nruns) {
-    Tile nxt = cur;
-    nxt.n0 += kTileKeys;
-    if (nxt.n0 >= nxt.end) nxt = first_tile(cur.r + 1);
-    const bool has_next = nxt.r < nruns;
-    if (has_next) issue_tile(nxt.n0, buf ^ 1);
+  while (r < nruns) {
+    // next tile
+    int r2 = r, start2 = start, end2 = end, n2 = n0 + kTileKeys;
+    if (n2 >= end2) {
+      ++r2;
+      if (r2 < nruns) {
+        start2 = s_lo[r2] * P;
+        end2 = (s_hi[r2] + 1) * P;
+        n2 = start2 & ~7;
+      }
+    }
+    if (r2 < nruns) issue_tile(n2, buf ^ 1);
 
     if (wave_active) {
       const unsigned char *kb_base = s_k[buf];
@@ -220,17 +241,17 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
         }
       }
-      // keys of this tile outside the run: [lo_rel, hi_rel) are valid
-      const int lo_rel = (int)(cur.start > cur.n0 ? cur.start - cur.n0 : 0);
-      const long long span = cur.end - cur.n0;
-      const int hi_rel = span < kTileKeys ? (int)span : kTileKeys;
+      // keys of this tile outside the run: only [lo_rel, hi_rel) are valid
+      const int lo_rel = start > n0 ? start - n0 : 0;
+      const int hi_rel = end - n0 < kTileKeys ? end - n0 : kTileKeys;
       if (lo_rel > 0 || hi_rel < kTileKeys) {
+        const int lo_l = lo_rel - g8, hi_l = hi_rel - g8;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kb + (i & 7) + 8 * g + 16 * (i >> 3);
-            if (key < lo_rel || key >= hi_rel) s[kb][i] = -INFINITY;
+            const int key = 32 * kb + (i & 7) + 16 * (i >> 3);  // minus this lane's 8g
+            if (key < lo_l || key >= hi_l) s[kb][i] = -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -238,24 +259,30 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m, mx * scale_log2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      {
+        const HalfPair pr = with_other_half(mx);
+        mx = fmaxf(pr.a, pr.b) * scale_log2;
+      }
+      // rescale only when some row of the wavefront found a new max
+      if (__builtin_amdgcn_ballot_w64(mx > m) != 0) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first tile
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+        m = m_new;
+      }
       f16x8 pf[4];
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], scale_log2, -m_use));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], scale_log2, -m));
           psum += p;
           pf[2 * kb + (i >> 3)][i & 7] = (_Float16)p;
         }
-      l = l * alpha + psum;
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      l += psum;
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) {
 #pragma unroll
@@ -270,11 +297,15 @@ __global__ void __launch_bounds__(kThreads) attn_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's tile loads have landed in LDS
     __syncthreads();
     buf ^= 1;
-    cur = nxt;
+    r = r2;
+    start = start2;
+    end = end2;
+    n0 = n2;
   }
 
   if (!wave_active) return;
-  const float l_tot = l + other_half(l);
+  const HalfPair lp = with_other_half(l);
+  const float l_tot = lp.a + lp.b;
   if (!row_ok) return;
   const long long orow = head * Nq + (long long)tq * P + my_prow;
   float inv, lse_v;
