@@ -4,8 +4,10 @@ A thin ctypes layer over the C ABI declared in include/fsa.h: it checks
 tensor dtypes/shapes, allocates outputs and workspaces with torch on the
 inputs' device, passes raw pointers and torch's current HIP stream, and turns
 a non-OK status into FsaError.  Every computation happens in the library's HIP
-kernels; there is no fallback.  Importing this module fails loudly when
-libfsa.so has not been built (python -m frame_sparse_attention_amd.build).
+kernels; there is no fallback.  The first library call raises ImportError
+when libfsa.so has not been built (python -m frame_sparse_attention_amd.build);
+the library is loaded lazily so that the build script in this package can
+run before it exists.
 
 Functions (same names as the C entry points, without the fsa_ prefix):
   frame_set_capacity, build_frame_sets, build_frame_sets_host,
@@ -49,11 +51,6 @@ class HeadPolicy(ctypes.Structure):
                  "lo", "hi")]
 
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m frame_sparse_attention_amd.build` (needs ROCm hipcc)")
-_lib = ctypes.CDLL(LIB_PATH)
-
 _i32, _i64, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t,
                               ctypes.c_void_p)
 _pi32 = ctypes.POINTER(ctypes.c_int32)
@@ -81,20 +78,40 @@ _SIGS = {
                                               _i32, _vp, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
     "fsa_merge_lse": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp]),
 }
-for _name, (_res, _args) in _SIGS.items():
-    _fn = getattr(_lib, _name)
-    _fn.restype = _res
-    _fn.argtypes = _args
-
 EXPORTED = tuple(_SIGS)
+_LIB = None
+
+
+def _load() -> ctypes.CDLL:
+    """The loaded libfsa.so (loaded on first use, so that the build script in
+    this package can run before the library exists).  Raises ImportError if
+    it has not been built: there is no fallback."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m frame_sparse_attention_amd.build` (needs ROCm hipcc)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def __getattr__(name):
+    if name == "_lib":
+        return _load()
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
 
 
 def abi_version() -> int:
-    return int(_lib.fsa_abi_version())
+    return int(_load().fsa_abi_version())
 
 
 def last_error() -> str:
-    return _lib.fsa_last_error().decode()
+    return _load().fsa_last_error().decode()
 
 
 def _check(status: int) -> None:
@@ -140,7 +157,7 @@ def _need_contig(*ts):
 def frame_set_capacity(policies, Tq: int, Tk: int, offset: int = 0, chunk: int = 1) -> int:
     """Smallest cap that holds every frame set the policies can produce."""
     out = ctypes.c_int32(0)
-    _check(_lib.fsa_frame_set_capacity(len(policies), _policies(policies), Tq, Tk, offset, chunk,
+    _check(_load().fsa_frame_set_capacity(len(policies), _policies(policies), Tq, Tk, offset, chunk,
                                        ctypes.byref(out)))
     return out.value
 
@@ -163,7 +180,7 @@ def build_frame_sets(policies, B: int, Tq: int, Tk: int, offset: int = 0, chunk:
             raise ValueError("selected must be int32 [B, H, groups, k]")
         _need_contig(selected)
         topk_k = selected.shape[3]
-    _check(_lib.fsa_build_frame_sets(B, H, Tq, Tk, offset, chunk, _policies(policies),
+    _check(_load().fsa_build_frame_sets(B, H, Tq, Tk, offset, chunk, _policies(policies),
                                      _ptr(selected), topk_k, cap, _ptr(idx), _ptr(cnt),
                                      _stream(idx.device)))
     return idx, cnt
@@ -181,7 +198,7 @@ def build_frame_sets_host(policies, B: int, Tq: int, Tk: int, offset: int = 0, c
     if selected is not None:
         selected = np.ascontiguousarray(selected, dtype=np.int32)
         topk_k = selected.shape[3]
-    _check(_lib.fsa_build_frame_sets_host(B, H, Tq, Tk, offset, chunk, _policies(policies),
+    _check(_load().fsa_build_frame_sets_host(B, H, Tq, Tk, offset, chunk, _policies(policies),
                                           _ptr(selected), topk_k, cap, _ptr(idx), _ptr(cnt)))
     return idx, cnt
 
@@ -191,7 +208,7 @@ def validate_frame_sets(idx, cnt, Tk: int) -> None:
     idx = np.ascontiguousarray(idx.cpu().numpy() if torch.is_tensor(idx) else idx, dtype=np.int32)
     cnt = np.ascontiguousarray(cnt.cpu().numpy() if torch.is_tensor(cnt) else cnt, dtype=np.int32)
     B, H, Tq, cap = idx.shape
-    _check(_lib.fsa_validate_frame_sets(B, H, Tq, Tk, cap, _ptr(idx), _ptr(cnt)))
+    _check(_load().fsa_validate_frame_sets(B, H, Tq, Tk, cap, _ptr(idx), _ptr(cnt)))
 
 
 # ----------------------------------------------------------------------------- top-k
@@ -213,10 +230,10 @@ def select_topk_frames(q: torch.Tensor, k: torch.Tensor, P: int, h_begin: int, h
         scores = torch.full((B, H, G, cand_end - cand_begin), float("nan"), dtype=torch.float64,
                             device=q.device)
     nbytes = ctypes.c_size_t(0)
-    _check(_lib.fsa_select_topk_workspace_size(B, H, Nq, D, P, q_group, cand_begin, cand_end,
+    _check(_load().fsa_select_topk_workspace_size(B, H, Nq, D, P, q_group, cand_begin, cand_end,
                                                ctypes.byref(nbytes)))
     ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)
-    _check(_lib.fsa_select_topk_frames(_ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P,
+    _check(_load().fsa_select_topk_frames(_ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P,
                                        h_begin, h_end, q_group, cand_begin, cand_end, topk,
                                        _ptr(out), _ptr(scores), _ptr(ws), nbytes.value,
                                        _stream(q.device)))
@@ -227,7 +244,7 @@ def select_topk_frames(q: torch.Tensor, k: torch.Tensor, P: int, h_begin: int, h
 def sparse_frame_attn_workspace_size(dtype, B: int, H: int, Nk: int, D: int) -> int:
     code = dtype if isinstance(dtype, int) else (BF16 if dtype == torch.bfloat16 else F32)
     out = ctypes.c_size_t(0)
-    _check(_lib.fsa_sparse_frame_attn_workspace_size(code, B, H, Nk, D, ctypes.byref(out)))
+    _check(_load().fsa_sparse_frame_attn_workspace_size(code, B, H, Nk, D, ctypes.byref(out)))
     return out.value
 
 
@@ -258,7 +275,7 @@ def sparse_frame_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: to
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.fsa_sparse_frame_attn(_ptr(q), _ptr(k), _ptr(v), dt, B, H, Nq, Nk, D, P,
+    _check(_load().fsa_sparse_frame_attn(_ptr(q), _ptr(k), _ptr(v), dt, B, H, Nq, Nk, D, P,
                                       _ptr(idx), _ptr(cnt), idx.shape[3],
                                       float(scale) if scale is not None else 0.0, _ptr(o),
                                       _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device)))
@@ -273,7 +290,7 @@ def prepare_values(v: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     need = sparse_frame_attn_workspace_size(_dtype_code(v), B, H, Nk, D)
     if out is None:
         out = torch.empty(max(1, need), dtype=torch.uint8, device=v.device)
-    _check(_lib.fsa_prepare_values(_ptr(v), _dtype_code(v), B, H, Nk, D, _ptr(out),
+    _check(_load().fsa_prepare_values(_ptr(v), _dtype_code(v), B, H, Nk, D, _ptr(out),
                                    out.numel() * out.element_size(), _stream(v.device)))
     return out
 
@@ -292,7 +309,7 @@ def sparse_frame_attn_prepared(q: torch.Tensor, k: torch.Tensor, prepared: torch
                                                 device=q.device)
     lse = out_lse if out_lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
                                                           device=q.device)
-    _check(_lib.fsa_sparse_frame_attn_prepared(
+    _check(_load().fsa_sparse_frame_attn_prepared(
         _ptr(q), _ptr(k), _ptr(prepared), _dtype_code(q), B, H, Nq, Nk, D, P, _ptr(idx),
         _ptr(cnt), idx.shape[3], float(scale) if scale is not None else 0.0, _ptr(o), _ptr(lse),
         prepared.numel() * prepared.element_size(), _stream(q.device)))
@@ -312,6 +329,6 @@ def merge_lse(o1: torch.Tensor, lse1: torch.Tensor, o2: torch.Tensor, lse2: torc
     rows = lse1.numel()
     o = out if out is not None else torch.empty_like(o1)
     lse = out_lse if out_lse is not None else torch.empty_like(lse1)
-    _check(_lib.fsa_merge_lse(_ptr(o1), _ptr(lse1), _ptr(o2), _ptr(lse2), rows, D, _ptr(o),
+    _check(_load().fsa_merge_lse(_ptr(o1), _ptr(lse1), _ptr(o2), _ptr(lse2), rows, D, _ptr(o),
                               _ptr(lse), _stream(o1.device)))
     return o, lse

@@ -152,3 +152,17 @@ def test_build_frame_sets_argument_errors():
         fsa.build_frame_sets_host([dict(kind=fsa.SINK_WINDOW, window=2)], 1, 4, 4, offset=1)
     with pytest.raises(fsa.FsaError, match="H=65"):
         fsa.build_frame_sets_host([dict(kind=fsa.FULL)] * 65, 1, 4, 4)
+
+
+def test_missing_library_fails_loudly_on_first_call(monkeypatch, tmp_path):
+    # the binding has no fallback: without libfsa.so the first call raises
+    monkeypatch.setattr(fsa, "LIB_PATH", str(tmp_path / "libfsa.so"))
+    monkeypatch.setattr(fsa, "_LIB", None)
+    with pytest.raises(ImportError, match="libfsa.so is missing"):
+        fsa.abi_version()
+
+
+def test_build_module_imports_without_the_library():
+    import importlib
+    mod = importlib.import_module("frame_sparse_attention_amd.build")
+    assert mod.ARCH == "gfx950" and "attn_bf16.hip" in mod.SOURCES
