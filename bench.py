@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "effective attention TFLOP/s (attended pairs) + % of bf16 MFMA peak, 1 GPU"
 KERNEL_SOURCES = ["frame_sparse_attention_amd/csrc/attn_bf16.hip",
                   "frame_sparse_attention_amd/csrc/attn_common.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_lvsa_T42_P1560_H12.traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_lvsa_T42_P1560_H12.traffic.txt")
 
 
 def kernel_source_hash() -> str:
@@ -42,17 +42,26 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(launch_units: int):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (already scaled by the copy-kernel
+    calibration), if they were taken on the current kernel source; else None.
+    The record is 'key: value' lines."""
+    rec = {}
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    rec[key.strip()] = val.strip()
+    except OSError:
         return None
     if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float):
@@ -92,6 +101,54 @@ def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float):
                       f"{dt:.1f} s"}
 
 
+def time_ms(fn, reps: int = 20) -> float:
+    """Average duration of fn() over reps launches, HIP events on the current stream."""
+    import torch
+    fn()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def aux_rows(dev):
+    """The other hot-path rows at their workload shapes, each against the HBM roof:
+    frame pooling + top-k (AR chunk, memory heads 8-11) and the LSE merge (the
+    decomposable workload's two branches)."""
+    import torch
+
+    import frame_sparse_attention_amd as fsa
+    import workloads as wl
+    out = {}
+    w = wl.ar_chunk()
+    q, k, _ = wl.make_qkv(w)
+    qd, kd = q.to(dev), k.to(dev)
+    sel = torch.empty((w.B, w.H, 1, 8), dtype=torch.int32, device=dev)
+    ms = time_ms(lambda: fsa.select_topk_frames(qd, kd, w.P, 8, 12, 3, 0, 57, 8, out=sel))
+    nbytes = 4 * (w.Nq + 57 * w.P) * w.D * 2      # every pooled bf16 element read once
+    out["select_topk_frames"] = {"workload": w.name, "ms": round(ms, 4),
+                                 "algorithmic_bytes": nbytes,
+                                 "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                 "frac_of_8TBps": round(nbytes / (ms * 1e-3) / 8e12, 4)}
+    del q, k, qd, kd
+    d = wl.decomposable()
+    rows = d.B * d.H * d.Nq
+    g = torch.Generator(device="cpu").manual_seed(4)
+    o1, o2 = (torch.randn(rows, d.D, generator=g).to(dev) for _ in range(2))
+    l1, l2 = (torch.randn(rows, generator=g).to(dev) for _ in range(2))
+    om, lm = torch.empty_like(o1), torch.empty_like(l1)
+    ms = time_ms(lambda: fsa.merge_lse(o1, l1, o2, l2, out=om, out_lse=lm))
+    nbytes = rows * (3 * d.D + 3) * 4
+    out["merge_lse"] = {"workload": d.name, "ms": round(ms, 4), "algorithmic_bytes": nbytes,
+                        "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_8TBps": round(nbytes / (ms * 1e-3) / 8e12, 4)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +156,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--no-aux", action="store_true",
+                    help="skip timing the top-k and merge rows at their own workload shapes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (reference "
                          "kernel for scaling HBM byte counters), then exit")
@@ -190,7 +249,7 @@ def main() -> int:
 
     value = flop_per_step / (ms_per_step * 1e-3) / 1e12
     achieved = flop_per_step / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic(1)
+    traffic = measured_traffic()
     qtiles = -(-w.P // 128)
     issued_pairs = w.B * w.H * w.Tq * qtiles * 128 * int(cnt[0, 0, 0].item()) * w.P
     out = {
@@ -219,6 +278,11 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    prep_bytes = w.B * w.H * w.Nk * w.D * 4        # read bf16 V, write fp16 copy
+    out["kernels_GB_per_s"] = {"prepare_values": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
+    if not args.no_aux:
+        print("[bench] top-k and merge rows", file=sys.stderr, flush=True)
+        out["aux"] = aux_rows(dev)
     if args.cpu_seconds > 0:
         print("[bench] CPU baseline (oracle)", file=sys.stderr, flush=True)
         # the baseline uses the frame sets of step 0

@@ -140,33 +140,34 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
   float m = -INFINITY;  // running row max, scaled base-2 units
-  float l = 0.f;        // running row sum against m (this lane's half of the keys)
+  float l = 0.f;        // running row sum (this lane's half of the keys)
 
-  const uint16_t *kh = k + head * (long long)Nk * D;
-  const _Float16 *vh = vt + head * (long long)NkC * D * 8;
+  const char *kh = reinterpret_cast<const char *>(k + head * (long long)Nk * D);
+  const char *vh = reinterpret_cast<const char *>(vt + head * (long long)NkC * D * 8);
 
   // Tile loads go straight from HBM into LDS (global_load_lds_dwordx4): each
   // wavefront instruction fills 64 consecutive 16-byte LDS units, one per
   // lane, and the lane picks the global chunk that belongs at its unit.
   // K: unit u -> slot u / NCH, stored chunk u % NCH, which holds logical chunk
   // (u % NCH) ^ (slot & SWZ) of key key_slot(slot).  V^T: unit u is the u-th
-  // 16-byte chunk of the tile, contiguous in the workspace.  Per-lane offsets
-  // are fixed; only the tile's base pointer changes.
-  int koff[KLD], kkey[KLD];
+  // 16-byte chunk of the tile, contiguous in the workspace.  The per-lane byte
+  // offsets are fixed; only the tile's (wave-uniform) base address changes.
+  unsigned koff[KLD];
+  int kkey[KLD];
 #pragma unroll
   for (int it = 0; it < KLD; ++it) {
     const int u = (it * 4 + wave) * 64 + lane;
     const int slot = u / NCH, pc = u % NCH;
     kkey[it] = key_slot(slot);
-    koff[it] = kkey[it] * D + (pc ^ (slot & SWZ)) * 8;
+    koff[it] = (unsigned)(kkey[it] * D + (pc ^ (slot & SWZ)) * 8) * 2u;
   }
-  auto issue_tile = [&](int n0, int bsel) {
-    const uint16_t *kbase = kh + (long long)n0 * D;
+  auto issue_k = [&](int n0, int bsel) {
+    const char *base = kh + (long long)n0 * D * 2;
     if (n0 + kTileKeys <= Nk) {
 #pragma unroll
       for (int it = 0; it < KLD; ++it)
         __builtin_amdgcn_global_load_lds(
-            (const void *)(kbase + koff[it]),
+            (const void *)(base + koff[it]),
             (__attribute__((address_space(3))) void *)&s_k[bsel][(it * 4 + wave) * 1024], 16, 0,
             0);
     } else {
@@ -174,76 +175,103 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
 #pragma unroll
       for (int it = 0; it < KLD; ++it) {
         const int over = n0 + kkey[it] - (Nk - 1);
-        const int off = over > 0 ? koff[it] - over * D : koff[it];
+        const unsigned off = over > 0 ? koff[it] - (unsigned)(over * D * 2) : koff[it];
         __builtin_amdgcn_global_load_lds(
-            (const void *)(kbase + off),
+            (const void *)(base + off),
             (__attribute__((address_space(3))) void *)&s_k[bsel][(it * 4 + wave) * 1024], 16, 0,
             0);
       }
     }
+  };
+  auto issue_v = [&](int n0, int bsel) {
     const int c0 = n0 / 8;
-    const _Float16 *vbase = vh + (long long)c0 * D * 8;
-    const bool v_whole = c0 + kTileKeys / 8 <= NkC;
+    const char *base = vh + (long long)c0 * D * 16;
+    const bool whole = c0 + kTileKeys / 8 <= NkC;
 #pragma unroll
     for (int it = 0; it < VLD; ++it) {
       const int u = (it * 4 + wave) * 64 + lane;
-      int off = u * 8;
-      if (!v_whole) {
+      unsigned off = (unsigned)u * 16u;
+      if (!whole) {
         const int over = c0 + u / D - (NkC - 1);
-        if (over > 0) off -= over * D * 8;
+        if (over > 0) off -= (unsigned)(over * D * 16);
       }
       __builtin_amdgcn_global_load_lds(
-          (const void *)(vbase + off),
+          (const void *)(base + off),
           (__attribute__((address_space(3))) void *)&s_v[bsel][(it * 4 + wave) * 1024], 16, 0, 0);
     }
   };
+  // S^T of one tile: 2 blocks of 32 keys x 32 query rows
+  auto qk = [&](int bsel, f32x16 *sacc) {
+    const unsigned char *kb_base = s_k[bsel];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+      const int slot = kb * 32 + j;
+      const unsigned char *krow = kb_base + slot * D * 2;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int c = 2 * ks + g;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + ((c ^ (slot & SWZ)) * 16));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+  };
 
-  // tile cursor: run r, run key range [start, end), tile start n0 (multiple of 8)
-  int r = 0, start = 0, end = 0, n0 = 0;
+  // Tile cursor.  The loop is software-pipelined: iteration i holds S of tile
+  // i (computed one iteration earlier) and issues the Q.K^T MFMAs of tile i+1
+  // next to the softmax of tile i, then the P.V MFMAs of tile i.  K and V
+  // each have two LDS slots, staggered: during iteration i, K of tile i+1 and
+  // V of tile i are read while K of tile i+2 and V of tile i+1 stream in.
+  struct Cur {
+    int r, start, end, n0;
+  };
+  auto advance = [&](Cur c) {
+    c.n0 += kTileKeys;
+    if (c.n0 >= c.end) {
+      ++c.r;
+      if (c.r < nruns) {
+        c.start = s_lo[c.r] * P;
+        c.end = (s_hi[c.r] + 1) * P;
+        c.n0 = c.start & ~7;
+      }
+    }
+    return c;
+  };
+  Cur cur{0, 0, 0, 0};
   if (nruns > 0) {
-    start = s_lo[0] * P;
-    end = (s_hi[0] + 1) * P;
-    n0 = start & ~7;
-    issue_tile(n0, 0);
+    cur.start = s_lo[0] * P;
+    cur.end = (s_hi[0] + 1) * P;
+    cur.n0 = cur.start & ~7;
+  }
+  Cur nxt = advance(cur);
+  int ks_slot = 0;  // K slot holding the tile whose S is computed next
+  if (nruns > 0) {
+    issue_k(cur.n0, 0);
+    issue_v(cur.n0, 0);
+    if (nxt.r < nruns) issue_k(nxt.n0, 1);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 
-  // per-lane key bounds are compared against compile-time key offsets
   const int g8 = 8 * g;
-  int buf = 0;
-  while (r < nruns) {
-    // next tile
-    int r2 = r, start2 = start, end2 = end, n2 = n0 + kTileKeys;
-    if (n2 >= end2) {
-      ++r2;
-      if (r2 < nruns) {
-        start2 = s_lo[r2] * P;
-        end2 = (s_hi[r2] + 1) * P;
-        n2 = start2 & ~7;
-      }
-    }
-    if (r2 < nruns) issue_tile(n2, buf ^ 1);
+  f32x16 sc[2];
+  if (wave_active && nruns > 0) qk(0, sc);
+  // every wave has read K slot 0 before iteration 0 streams tile 2 into it
+  __syncthreads();
+  int vs = 0;  // V slot of the current tile
+  // One tile: scur holds S of tile i, snext receives S of tile i+1.  The loop
+  // below unrolls by two and swaps the roles of the two register sets, so S
+  // never has to be copied from one to the other.
+  auto step = [&](f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+    const Cur nn = advance(nxt);  // tile i+2
+    const bool has_next = nxt.r < nruns;
+    if (nn.r < nruns) issue_k(nn.n0, vs);        // K slot of tile i is free now
+    if (has_next) issue_v(nxt.n0, vs ^ 1);       // V slot of tile i-1 is free now
 
     if (wave_active) {
-      const unsigned char *kb_base = s_k[buf];
-      const unsigned char *vb_base = s_v[buf];
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int slot = kb * 32 + j;
-        const unsigned char *krow = kb_base + slot * D * 2;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const int c = 2 * ks + g;
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + ((c ^ (slot & SWZ)) * 16));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-        }
-      }
       // keys of this tile outside the run: only [lo_rel, hi_rel) are valid
-      const int lo_rel = start > n0 ? start - n0 : 0;
-      const int hi_rel = end - n0 < kTileKeys ? end - n0 : kTileKeys;
+      const int lo_rel = cur.start > cur.n0 ? cur.start - cur.n0 : 0;
+      const int hi_rel = cur.end - cur.n0 < kTileKeys ? cur.end - cur.n0 : kTileKeys;
       if (lo_rel > 0 || hi_rel < kTileKeys) {
         const int lo_l = lo_rel - g8, hi_l = hi_rel - g8;
 #pragma unroll
@@ -251,14 +279,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = 32 * kb + (i & 7) + 16 * (i >> 3);  // minus this lane's 8g
-            if (key < lo_l || key >= hi_l) s[kb][i] = -INFINITY;
+            if (key < lo_l || key >= hi_l) scur[kb][i] = -INFINITY;
           }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, scur[kb][i]);
       {
         const HalfPair pr = with_other_half(mx);
         mx = fmaxf(pr.a, pr.b) * scale_log2;
@@ -272,17 +300,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
         for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
         m = m_new;
       }
+      // Q.K^T of the next tile (on a stale slot after the last tile: unused)
+      qk(ks_slot ^ 1, snext);
       f16x8 pf[4];
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], scale_log2, -m));
+          const float p = __builtin_amdgcn_exp2f(fmaf(scur[kb][i], scale_log2, -m));
           psum += p;
           pf[2 * kb + (i >> 3)][i & 7] = (_Float16)p;
         }
       l += psum;
+      const unsigned char *vb_base = s_v[vs];
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) {
 #pragma unroll
@@ -296,11 +327,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's tile loads have landed in LDS
     __syncthreads();
-    buf ^= 1;
-    r = r2;
-    start = start2;
-    end = end2;
-    n0 = n2;
+    ks_slot ^= 1;
+    vs ^= 1;
+    cur = nxt;
+    nxt = nn;
+  };
+  f32x16 sd[2];
+  while (cur.r < nruns) {
+    step(sc, sd);
+    if (cur.r >= nruns) break;
+    step(sd, sc);
   }
 
   if (!wave_active) return;
