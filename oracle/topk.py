@@ -13,8 +13,12 @@ Readings (the pages fix neither the arithmetic nor the tie rule):
   * pooling is kept as float64 sums; a mean differs from the sum by a positive
     factor, so the ranking is the same under exact arithmetic and no division
     enters the bits;
-  * qsum[d]   = Σ_i Q[i, d] over the group's query tokens, added one at a time
-                in ascending token order, in float64;
+  * qf[t,d]   = Σ_p Q[t·P + p, d]: queries are compressed to frame
+                granularity first, like the keys, added one at a time in
+                ascending p;
+  * qsum[d]   = Σ_t qf[t, d] over the frames of the query group, added one at
+                a time in ascending frame order (in exact arithmetic: the sum
+                over all of the group's tokens);
   * ksum[f,d] = Σ_p K[f·P + p, d], added one at a time in ascending p;
   * score[f]  = Σ_d qsum[d] · ksum[f, d], each product rounded to float64 and
                 then added one at a time in ascending d (no fused multiply-add);
@@ -29,16 +33,19 @@ from __future__ import annotations
 import numpy as np
 
 
-def pooled_query_sum(q_tokens: np.ndarray) -> np.ndarray:
-    """qsum[d]: float64 sum of the query tokens, sequential in token order.
-
-    q_tokens [N, D].  The loop runs over tokens; numpy's elementwise add rounds
-    each d separately, so every qsum[d] is a strictly sequential sum.
-    """
+def pooled_query_sum(q_tokens: np.ndarray, P: int) -> np.ndarray:
+    """qsum[d] of a query group given as whole frames of P tokens (q_tokens [F·P, D]):
+    each frame summed sequentially over its tokens, then the frame sums added
+    sequentially in frame order (all in float64)."""
     q = np.asarray(q_tokens, dtype=np.float64)
+    if q.shape[0] % P:
+        raise ValueError("a query group is made of whole frames")
     acc = np.zeros(q.shape[1], dtype=np.float64)
-    for i in range(q.shape[0]):
-        acc = acc + q[i]
+    for f in range(q.shape[0] // P):
+        frame = np.zeros(q.shape[1], dtype=np.float64)
+        for p in range(P):
+            frame = frame + q[f * P + p]
+        acc = acc + frame
     return acc
 
 
@@ -76,11 +83,12 @@ def select_topk_frames(q_bh: np.ndarray, k_bh: np.ndarray, P: int, q_rows,
                        cand_frames, k: int):
     """Top-k frames of one (b, h, query group).
 
-    q_bh [Nq, D], k_bh [Nk, D]; q_rows are the token indices pooled into the
-    query; cand_frames the KV frames that may be chosen.
+    q_bh [Nq, D], k_bh [Nk, D]; q_rows are the token indices of the query
+    group's frames (whole frames, in order); cand_frames the KV frames that may
+    be chosen.
     Returns (sorted frames, scores of every candidate).
     """
-    qsum = pooled_query_sum(np.asarray(q_bh)[np.asarray(q_rows)])
+    qsum = pooled_query_sum(np.asarray(q_bh)[np.asarray(q_rows)], P)
     ksum = pooled_key_sums(k_bh, P, cand_frames)
     scores = frame_scores(qsum, ksum)
     return rank_topk(scores, cand_frames, k), scores

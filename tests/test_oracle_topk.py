@@ -17,7 +17,7 @@ from oracle import topk
 
 def test_planted_frames_rank_by_alignment():
     # every query token equals u; frame f's tokens all equal c_f·u
-    D, P, Nq = 8, 5, 7
+    D, P, Nq = 8, 5, 10
     u = np.arange(1, D + 1, dtype=np.float64)
     c = [3, -1, 7, 0, 5, 2, 7.5, -4]
     q = np.tile(u, (Nq, 1))
@@ -28,6 +28,7 @@ def test_planted_frames_rank_by_alignment():
 
 
 def _exact_scores(q, k, P, rows, cands):
+    # exact rational sums: any summation order gives these values
     qs = [sum(Fraction(float(q[i, d])) for i in rows) for d in range(q.shape[1])]
     out = []
     for f in cands:
@@ -39,7 +40,7 @@ def _exact_scores(q, k, P, rows, cands):
 @pytest.mark.parametrize("seed", range(6))
 def test_matches_exact_arithmetic_ranking(seed):
     rng = np.random.default_rng(seed)
-    D, P, F, Nq, kk = 16, 6, 12, 9, 4
+    D, P, F, Nq, kk = 16, 6, 12, 12, 4
     q = rng.standard_normal((Nq, D)).astype(np.float32).astype(np.float64)
     k = rng.standard_normal((F * P, D)).astype(np.float32).astype(np.float64)
     frames, scores = topk.select_topk_frames(q, k, P, range(Nq), range(F), kk)
@@ -53,11 +54,15 @@ def test_matches_exact_arithmetic_ranking(seed):
         assert abs(scores[f] - float(exact[f])) <= 1e-9 * max(1.0, abs(float(exact[f])))
 
 
-def test_query_pooling_is_sequential_in_token_order():
-    # 1e16 + 1 rounds back to 1e16 (spacing 2): sequential gives ((1e16+1)-1e16)+1 = 1,
-    # a pairwise sum gives (1e16+1) + (-1e16+1) = 0, the exact sum is 2.
+def test_query_pooling_is_frames_first_then_sequential():
+    # 1e16 + 1 rounds back to 1e16 (spacing 2).  One frame of 4 tokens:
+    # ((1e16+1)-1e16)+1 = 1.  Two frames of 2 tokens: frame sums 1e16 and -1e16,
+    # total 0 (a token-sequential order would give 1; the exact sum is 2).
     q = np.array([[1e16], [1.0], [-1e16], [1.0]])
-    assert topk.pooled_query_sum(q).tolist() == [1.0]
+    assert topk.pooled_query_sum(q, 4).tolist() == [1.0]
+    assert topk.pooled_query_sum(q, 2).tolist() == [0.0]
+    with pytest.raises(ValueError):
+        topk.pooled_query_sum(q, 3)
 
 
 def test_key_pooling_is_sequential_in_p():
@@ -82,19 +87,19 @@ def test_scores_sum_sequentially_in_d():
 
 def test_ties_go_to_the_earlier_frame():
     D, P = 4, 3
-    q = np.ones((2, D))
+    q = np.ones((3, D))
     base = np.ones((P, D))
     k = np.concatenate([base * 2, base, base * 2, base * 2, base])
-    frames, _ = topk.select_topk_frames(q, k, P, range(2), range(5), 2)
+    frames, _ = topk.select_topk_frames(q, k, P, range(3), range(5), 2)
     assert frames == [0, 2]
 
 
 def test_positive_scaling_of_queries_keeps_the_selection():
     rng = np.random.default_rng(7)
-    q = rng.standard_normal((10, 8))
+    q = rng.standard_normal((12, 8))
     k = rng.standard_normal((8 * 4, 8))
-    a, _ = topk.select_topk_frames(q, k, 4, range(10), range(8), 3)
-    b, _ = topk.select_topk_frames(q * 4.0, k, 4, range(10), range(8), 3)
+    a, _ = topk.select_topk_frames(q, k, 4, range(12), range(8), 3)
+    b, _ = topk.select_topk_frames(q * 4.0, k, 4, range(12), range(8), 3)
     assert a == b
 
 
@@ -106,5 +111,7 @@ def test_candidate_subset_and_errors():
     assert frames == [1, 3, 4] and scores.shape == (3,)
     with pytest.raises(ValueError):
         topk.select_topk_frames(q, k, 2, range(4), [1, 3], 3)
+    with pytest.raises(ValueError):
+        topk.select_topk_frames(q, k, 2, range(3), [1, 3], 1)
     with pytest.raises(ValueError):
         topk.rank_topk(np.array([1.0, np.nan]), [0, 1], 1)
