@@ -146,6 +146,26 @@ def aux_rows(dev):
     out["merge_lse"] = {"workload": d.name, "ms": round(ms, 4), "algorithmic_bytes": nbytes,
                         "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                         "frac_of_8TBps": round(nbytes / (ms * 1e-3) / 8e12, 4)}
+    del o1, o2, l1, l2, om, lm
+    # decomposable attention: local (sink + chunk) and full (49 frames) outputs,
+    # single pass vs branch A + branch B + merge
+    q, k, v = (t.to(dev) for t in wl.make_qkv(d))
+    lists = {n: fsa.build_frame_sets(d.branches[n], d.B, d.Tq, d.Tk, d.offset, d.chunk,
+                                     device=dev) for n in ("A", "B")}
+    prep = fsa.prepare_values(v)
+
+    def two_branches():
+        oa, la = fsa.sparse_frame_attn_prepared(q, k, prep, *lists["A"], d.P)
+        ob, lb = fsa.sparse_frame_attn_prepared(q, k, prep, *lists["B"], d.P)
+        fsa.merge_lse(oa, la, ob, lb)
+
+    ms_dual = time_ms(lambda: fsa.sparse_frame_attn_dual(q, k, prep, *lists["A"], *lists["B"],
+                                                         d.P), 10)
+    ms_three = time_ms(two_branches, 10)
+    pairs = d.B * d.H * d.Nq * 49 * d.P
+    out["dual_pass"] = {"workload": d.name, "ms_single_pass": round(ms_dual, 4),
+                        "ms_two_branches_plus_merge": round(ms_three, 4),
+                        "effective_TFLOP_per_s": round(4 * d.D * pairs / (ms_dual * 1e-3) / 1e12, 1)}
     return out
 
 

@@ -12,7 +12,7 @@ run before it exists.
 Functions (same names as the C entry points, without the fsa_ prefix):
   frame_set_capacity, build_frame_sets, build_frame_sets_host,
   validate_frame_sets, select_topk_frames, sparse_frame_attn, prepare_values,
-  sparse_frame_attn_prepared, merge_lse,
+  sparse_frame_attn_prepared, sparse_frame_attn_dual, merge_lse,
   plus the workspace-size queries, abi_version and last_error.
 """
 
@@ -76,6 +76,9 @@ _SIGS = {
     "fsa_prepare_values": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "fsa_sparse_frame_attn_prepared": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _i32, _vp, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
+    "fsa_sparse_frame_attn_dual_prepared": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                   _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32,
+                                                   _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fsa_merge_lse": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp]),
 }
 EXPORTED = tuple(_SIGS)
@@ -314,6 +317,24 @@ def sparse_frame_attn_prepared(q: torch.Tensor, k: torch.Tensor, prepared: torch
         _ptr(cnt), idx.shape[3], float(scale) if scale is not None else 0.0, _ptr(o), _ptr(lse),
         prepared.numel() * prepared.element_size(), _stream(q.device)))
     return o, lse
+
+
+def sparse_frame_attn_dual(q: torch.Tensor, k: torch.Tensor, prepared: torch.Tensor,
+                           idx_a: torch.Tensor, cnt_a: torch.Tensor, idx_b: torch.Tensor,
+                           cnt_b: torch.Tensor, P: int, scale: float | None = None):
+    """One pass over frame lists A then B: returns (O_A, LSE_A, O_AB, LSE_AB),
+    attention over A alone and over A and B together (disjoint lists)."""
+    _need_contig(q, k, prepared, idx_a, cnt_a, idx_b, cnt_b)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    outs = [torch.empty((B, H, Nq, D), dtype=torch.float32, device=q.device) for _ in range(2)]
+    lses = [torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) for _ in range(2)]
+    _check(_load().fsa_sparse_frame_attn_dual_prepared(
+        _ptr(q), _ptr(k), _ptr(prepared), _dtype_code(q), B, H, Nq, Nk, D, P, _ptr(idx_a),
+        _ptr(cnt_a), idx_a.shape[3], _ptr(idx_b), _ptr(cnt_b), idx_b.shape[3],
+        float(scale) if scale is not None else 0.0, _ptr(outs[0]), _ptr(lses[0]), _ptr(outs[1]),
+        _ptr(lses[1]), prepared.numel() * prepared.element_size(), _stream(q.device)))
+    return outs[0], lses[0], outs[1], lses[1]
 
 
 def merge_lse(o1: torch.Tensor, lse1: torch.Tensor, o2: torch.Tensor, lse2: torch.Tensor,

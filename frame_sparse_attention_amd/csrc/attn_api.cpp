@@ -11,13 +11,17 @@ fsa_status launch_attn_f32(const float *q, const float *k, const float *v, const
 fsa_status launch_prepare_values_bf16(const void *v, int B, int H, int Nk, int D, void *prepared,
                                       hipStream_t stream);
 fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *prepared,
-                                     const int32_t *idx, const int32_t *cnt, int cap, int B,
-                                     int H, int Nq, int Nk, int D, int P, float scale, float *o,
-                                     float *lse, hipStream_t stream);
+                                     const int32_t *idx, const int32_t *cnt, int cap,
+                                     const int32_t *idx_b, const int32_t *cnt_b, int cap_b,
+                                     int B, int H, int Nq, int Nk, int D, int P, float scale,
+                                     float *o_first, float *lse_first, float *o, float *lse,
+                                     hipStream_t stream);
 size_t attn_bf16_workspace(long long heads, int Nk, int D);
 }  // namespace fsa
 
 namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 fsa_status check_common(int32_t dt, int32_t B, int32_t H, int32_t Nk, int32_t D) {
   FSA_REQUIRE(dt == FSA_F32 || dt == FSA_BF16, FSA_E_DTYPE, "unknown dtype %d", dt);
@@ -71,6 +75,8 @@ extern "C" fsa_status fsa_prepare_values(const void *v, int32_t dt, int32_t B, i
   const size_t need = fsa::attn_bf16_workspace((long long)B * H, Nk, D);
   if (need == 0) return FSA_OK;
   FSA_REQUIRE(v && prepared, FSA_E_ARG, "null pointer argument");
+  FSA_REQUIRE(aligned16(v) && aligned16(prepared), FSA_E_ARG,
+              "v and the prepared buffer must be 16-byte aligned");
   FSA_REQUIRE(prepared_bytes >= need, FSA_E_CAPACITY, "prepared buffer of %zu bytes < %zu needed",
               prepared_bytes, need);
   return fsa::launch_prepare_values_bf16(v, B, H, Nk, D, prepared, fsa::as_stream(stream));
@@ -89,9 +95,39 @@ extern "C" fsa_status fsa_sparse_frame_attn_prepared(
   FSA_REQUIRE(need == 0 || prepared, FSA_E_ARG, "k or v is NULL");
   FSA_REQUIRE(prepared_bytes >= need, FSA_E_CAPACITY, "prepared buffer of %zu bytes < %zu needed",
               prepared_bytes, need);
+  FSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(prepared) && aligned16(o), FSA_E_ARG,
+              "q, k, o and the prepared buffer must be 16-byte aligned");
   if (scale <= 0.f) scale = 1.f / std::sqrt((float)D);
-  return fsa::launch_attn_bf16_prepared(q, k, prepared, idx, cnt, cap, B, H, Nq, Nk, D, P, scale,
-                                        o, lse, fsa::as_stream(stream));
+  return fsa::launch_attn_bf16_prepared(q, k, prepared, idx, cnt, cap, nullptr, nullptr, 0, B, H,
+                                        Nq, Nk, D, P, scale, nullptr, nullptr, o, lse,
+                                        fsa::as_stream(stream));
+}
+
+extern "C" fsa_status fsa_sparse_frame_attn_dual_prepared(
+    const void *q, const void *k, const void *prepared, int32_t dt, int32_t B, int32_t H,
+    int32_t Nq, int32_t Nk, int32_t D, int32_t P, const int32_t *idx_a, const int32_t *cnt_a,
+    int32_t cap_a, const int32_t *idx_b, const int32_t *cnt_b, int32_t cap_b, float scale,
+    float *o_a, float *lse_a, float *o_ab, float *lse_ab, size_t prepared_bytes, void *stream) {
+  fsa::clear_error();
+  bool skip = false;
+  fsa_status st =
+      check_attn(q, k, dt, B, H, Nq, Nk, D, P, idx_a, cnt_a, cap_a, scale, o_ab, lse_ab, &skip);
+  if (st != FSA_OK || skip) return st;
+  FSA_REQUIRE(dt == FSA_BF16, FSA_E_DTYPE, "prepared values exist for bf16 only");
+  FSA_REQUIRE(idx_b && cnt_b && o_a && lse_a, FSA_E_ARG, "null pointer argument");
+  FSA_REQUIRE(cap_b >= 1 && cap_a + cap_b <= FSA_MAX_CAP, FSA_E_CAPACITY,
+              "cap_a + cap_b = %d outside [2, %d]", cap_a + cap_b, FSA_MAX_CAP);
+  const size_t need = fsa::attn_bf16_workspace((long long)B * H, Nk, D);
+  FSA_REQUIRE(need == 0 || prepared, FSA_E_ARG, "k or v is NULL");
+  FSA_REQUIRE(prepared_bytes >= need, FSA_E_CAPACITY, "prepared buffer of %zu bytes < %zu needed",
+              prepared_bytes, need);
+  FSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(prepared) && aligned16(o_a) &&
+                  aligned16(o_ab),
+              FSA_E_ARG, "q, k, the outputs and the prepared buffer must be 16-byte aligned");
+  if (scale <= 0.f) scale = 1.f / std::sqrt((float)D);
+  return fsa::launch_attn_bf16_prepared(q, k, prepared, idx_a, cnt_a, cap_a, idx_b, cnt_b, cap_b,
+                                        B, H, Nq, Nk, D, P, scale, o_a, lse_a, o_ab, lse_ab,
+                                        fsa::as_stream(stream));
 }
 
 extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const void *v,
@@ -115,10 +151,13 @@ extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const 
   FSA_REQUIRE(need == 0 || workspace != nullptr, FSA_E_ARG, "workspace is NULL");
   FSA_REQUIRE(workspace_bytes >= need, FSA_E_CAPACITY, "workspace of %zu bytes < %zu needed",
               workspace_bytes, need);
+  FSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) &&
+                  aligned16(workspace),
+              FSA_E_ARG, "q, k, v, o and the workspace must be 16-byte aligned (bf16 path)");
   if (need > 0) {
     st = fsa::launch_prepare_values_bf16(v, B, H, Nk, D, workspace, s);
     if (st != FSA_OK) return st;
   }
-  return fsa::launch_attn_bf16_prepared(q, k, workspace, idx, cnt, cap, B, H, Nq, Nk, D, P,
-                                        scale, o, lse, s);
+  return fsa::launch_attn_bf16_prepared(q, k, workspace, idx, cnt, cap, nullptr, nullptr, 0, B, H,
+                                        Nq, Nk, D, P, scale, nullptr, nullptr, o, lse, s);
 }

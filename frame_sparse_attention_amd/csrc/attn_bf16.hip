@@ -43,29 +43,41 @@ constexpr float kLn2 = 0.6931471805599453f;
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kWaitVm0 = 0x0F70;
 
-__device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
 // ---------------------------------------------------------------------------
 // V prepass: Vt[head][kc][d][e] = float16(V[head][8*kc + e][d]), zero past Nk.
-// One thread per (head, kc, d); each reads 8 rows (coalesced across d) and
-// writes 16 contiguous bytes.
-__global__ void __launch_bounds__(256) v_to_f16_chunked_kernel(
-    const uint16_t *__restrict__ v, _Float16 *__restrict__ vt, long long total, int Nk, int NkC,
-    int D) {
-  const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (u >= total) return;
-  const int d = (int)(u % D);
-  const long long hk = u / D;
-  const int kc = (int)(hk % NkC);
-  const long long hd = hk / NkC;
-  const uint16_t *src = v + (hd * Nk) * D + d;
-  f16x8 out;
+// One block per (head, 64 keys): 16-byte coalesced loads of the [64][D] bf16
+// tile, conversion to float16 into LDS, then 16-byte coalesced stores of the
+// [8 chunks][D][8] image (HBM-bound: 2 bytes read + 2 written per element).
+template <int D>
+__global__ void __launch_bounds__(256) v_to_f16_chunked_kernel(const uint16_t *__restrict__ v,
+                                                               _Float16 *__restrict__ vt,
+                                                               int Nk, int NkC) {
+  constexpr int kKeys = 64, NCH = D / 8;
+  __shared__ _Float16 tile[kKeys][D + 2];  // +2: rows start on different banks
+  const long long head = blockIdx.y;
+  const int key0 = blockIdx.x * kKeys;
+  const uint16_t *src = v + (head * Nk + key0) * D;
+  for (int u = threadIdx.x; u < kKeys * NCH; u += 256) {
+    const int kk = u / NCH, c = u % NCH;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (key0 + kk < Nk) raw = *reinterpret_cast<const uint4 *>(src + kk * D + c * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int n = kc * 8 + e;
-    out[e] = (_Float16)(n < Nk ? bf16_bits_to_float(src[(long long)n * D]) : 0.f);
+    for (int e = 0; e < 4; ++e) {
+      tile[kk][c * 8 + 2 * e] = (_Float16)__uint_as_float(w[e] << 16);
+      tile[kk][c * 8 + 2 * e + 1] = (_Float16)__uint_as_float(w[e] & 0xffff0000u);
+    }
   }
-  *reinterpret_cast<f16x8 *>(vt + u * 8) = out;
+  __syncthreads();
+  const int c0 = key0 / 8;
+  for (int u = threadIdx.x; u < (kKeys / 8) * D; u += 256) {
+    const int kc = u / D, d = u % D;
+    if (c0 + kc >= NkC) break;
+    f16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = tile[kc * 8 + e][d];
+    *reinterpret_cast<f16x8 *>(vt + ((head * NkC + c0 + kc) * D + d) * 8) = out;
+  }
 }
 
 // Slot of a key inside a 64-key K tile: bits 2 and 3 swapped (an involution).
@@ -89,12 +101,27 @@ __device__ inline HalfPair with_other_half(float x) {
   return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
-template <int D>
+// A frame-list argument (idx [B][H][Tq][cap], cnt [B][H][Tq]) and an output pair.
+struct ListArg {
+  const int32_t *idx;
+  const int32_t *cnt;
+  int cap;
+};
+struct OutArg {
+  float *o;
+  float *lse;
+};
+
+// DUAL = false: attention over the frames of list `la`, written to `all`.
+// DUAL = true: one pass over the runs of `la` followed by the runs of `lb`
+// with a single running softmax state; after the last tile of `la` the state
+// is written to `first` (attention over A alone), at the end to `all`
+// (attention over A and B together, exact when the two lists are disjoint).
+template <int D, bool DUAL>
 __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const _Float16 *__restrict__ vt, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ cnt, int cap, int H, int Nq, int Nk, int NkC, int P, int Tq,
-    int qtiles, float scale_log2, float *__restrict__ o, float *__restrict__ lse) {
+    const _Float16 *__restrict__ vt, ListArg la, ListArg lb, int H, int Nq, int Nk, int NkC,
+    int P, int Tq, int qtiles, float scale_log2, OutArg first, OutArg all) {
   constexpr int NCH = D / 8;                 // 16-byte chunks per K row
   constexpr int KBYTES = kTileKeys * D * 2;  // one K tile
   constexpr int VBYTES = (kTileKeys / 8) * D * 16;
@@ -104,7 +131,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char s_k[2][KBYTES];
   __shared__ __attribute__((aligned(16))) unsigned char s_v[2][VBYTES];
   __shared__ int s_lo[FSA_MAX_CAP], s_hi[FSA_MAX_CAP];
-  __shared__ int s_nruns;
+  __shared__ int s_nruns[2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -120,7 +147,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
   const long long head = (long long)b * H + h;
   const long long list = head * Tq + tq;
   const int Tk = Nk / P;
-  const int nruns = build_runs(idx + list * cap, cnt[list], cap, Tk, RunList{s_lo, s_hi}, &s_nruns);
+  // runs of list A, then (DUAL) the runs of list B after them
+  const int nruns_a =
+      build_runs(la.idx + list * la.cap, la.cnt[list], la.cap, Tk, RunList{s_lo, s_hi}, &s_nruns[0]);
+  int nruns = nruns_a;
+  if (DUAL)
+    nruns += build_runs(lb.idx + list * lb.cap, lb.cnt[list], lb.cap, Tk,
+                        RunList{s_lo + nruns_a, s_hi + nruns_a}, &s_nruns[1]);
 
   const int prow0 = qt * kRows + wave * kRowsPerWave;  // first row of this wave in the frame
   const bool wave_active = prow0 < P;
@@ -258,6 +291,34 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
   if (wave_active && nruns > 0) qk(0, sc);
   // every wave has read K slot 0 before iteration 0 streams tile 2 into it
   __syncthreads();
+  // O = acc / l and LSE = (m + log2 l) ln 2 of this wave's rows, written to `out`
+  auto store_out = [&](OutArg out) {
+    const HalfPair lp = with_other_half(l);
+    const float l_tot = lp.a + lp.b;
+    if (!row_ok) return;
+    const long long orow = head * Nq + (long long)tq * P + my_prow;
+    float inv, lse_v;
+    if (l_tot > 0.f) {
+      inv = 1.f / l_tot;
+      lse_v = (m + __log2f(l_tot)) * kLn2;
+    } else {
+      inv = 0.f;
+      lse_v = -INFINITY;
+    }
+    float *op = out.o + orow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 val;
+        val.x = acc[db][4 * q4 + 0] * inv;
+        val.y = acc[db][4 * q4 + 1] * inv;
+        val.z = acc[db][4 * q4 + 2] * inv;
+        val.w = acc[db][4 * q4 + 3] * inv;
+        *reinterpret_cast<float4 *>(op + db * 32 + 8 * q4 + 4 * g) = val;
+      }
+    if (g == 0) out.lse[orow] = lse_v;
+  };
   int vs = 0;  // V slot of the current tile
   // One tile: scur holds S of tile i, snext receives S of tile i+1.  The loop
   // below unrolls by two and swaps the roles of the two register sets, so S
@@ -323,6 +384,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ms], acc[db], 0, 0, 0);
         }
       }
+      // the last tile of list A: its state is the attention over A alone
+      if (DUAL && cur.r < nruns_a && nxt.r >= nruns_a) store_out(first);
     }
 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's tile loads have landed in LDS
@@ -333,38 +396,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
     nxt = nn;
   };
   f32x16 sd[2];
+  if (DUAL && wave_active && nruns_a == 0) store_out(first);
   while (cur.r < nruns) {
     step(sc, sd);
     if (cur.r >= nruns) break;
     step(sd, sc);
   }
-
-  if (!wave_active) return;
-  const HalfPair lp = with_other_half(l);
-  const float l_tot = lp.a + lp.b;
-  if (!row_ok) return;
-  const long long orow = head * Nq + (long long)tq * P + my_prow;
-  float inv, lse_v;
-  if (l_tot > 0.f) {
-    inv = 1.f / l_tot;
-    lse_v = (m + __log2f(l_tot)) * kLn2;
-  } else {
-    inv = 0.f;
-    lse_v = -INFINITY;
-  }
-  float *op = o + orow * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float4 val;
-      val.x = acc[db][4 * q4 + 0] * inv;
-      val.y = acc[db][4 * q4 + 1] * inv;
-      val.z = acc[db][4 * q4 + 2] * inv;
-      val.w = acc[db][4 * q4 + 3] * inv;
-      *reinterpret_cast<float4 *>(op + db * 32 + 8 * q4 + 4 * g) = val;
-    }
-  if (g == 0) lse[orow] = lse_v;
+  if (wave_active) store_out(all);
 }
 
 }  // namespace
@@ -379,19 +417,23 @@ fsa_status launch_prepare_values_bf16(const void *v, int B, int H, int Nk, int D
   const long long heads = (long long)B * H;
   const int NkC = (Nk + 7) / 8;
   if (NkC == 0 || heads == 0) return FSA_OK;
-  const long long total = heads * NkC * D;
-  const long long blocks = (total + 255) / 256;
-  FSA_REQUIRE(blocks < (1LL << 31), FSA_E_SHAPE, "V too large (%lld blocks)", blocks);
-  hipLaunchKernelGGL(v_to_f16_chunked_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t *>(v), static_cast<_Float16 *>(prepared), total,
-                     Nk, NkC, D);
+  FSA_REQUIRE(heads < 65536, FSA_E_SHAPE, "B*H=%lld exceeds 65535", heads);
+  const dim3 grid((unsigned)((Nk + 63) / 64), (unsigned)heads);
+  auto vv = static_cast<const uint16_t *>(v);
+  auto out = static_cast<_Float16 *>(prepared);
+  if (D == 64)
+    hipLaunchKernelGGL(v_to_f16_chunked_kernel<64>, grid, dim3(256), 0, stream, vv, out, Nk, NkC);
+  else
+    hipLaunchKernelGGL(v_to_f16_chunked_kernel<128>, grid, dim3(256), 0, stream, vv, out, Nk, NkC);
   return check_launch("prepare_values");
 }
 
 fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *prepared,
-                                     const int32_t *idx, const int32_t *cnt, int cap, int B,
-                                     int H, int Nq, int Nk, int D, int P, float scale, float *o,
-                                     float *lse, hipStream_t stream) {
+                                     const int32_t *idx, const int32_t *cnt, int cap,
+                                     const int32_t *idx_b, const int32_t *cnt_b, int cap_b,
+                                     int B, int H, int Nq, int Nk, int D, int P, float scale,
+                                     float *o_first, float *lse_first, float *o, float *lse,
+                                     hipStream_t stream) {
   const long long heads = (long long)B * H;
   const int NkC = (Nk + 7) / 8;
   const int Tq = Nq / P;
@@ -402,15 +444,26 @@ fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *p
   auto qq = static_cast<const uint16_t *>(q);
   auto kk = static_cast<const uint16_t *>(k);
   auto vt = static_cast<const _Float16 *>(prepared);
-  if (D == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       qq, kk, vt, idx, cnt, cap, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, o,
-                       lse);
-  else
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       qq, kk, vt, idx, cnt, cap, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, o,
-                       lse);
-  return check_launch("sparse_frame_attn (bf16)");
+  const ListArg la{idx, cnt, cap}, lb{idx_b, cnt_b, cap_b};
+  const OutArg first{o_first, lse_first}, all{o, lse};
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  const bool dual = idx_b != nullptr;
+  if (D == 64) {
+    if (dual)
+      hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, block, 0, stream, qq, kk, vt, la, lb,
+                         H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, block, 0, stream, qq, kk, vt, la,
+                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all);
+  } else {
+    if (dual)
+      hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, block, 0, stream, qq, kk, vt, la,
+                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, block, 0, stream, qq, kk, vt, la,
+                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all);
+  }
+  return check_launch(dual ? "sparse_frame_attn_dual (bf16)" : "sparse_frame_attn (bf16)");
 }
 
 }  // namespace fsa

@@ -168,8 +168,9 @@ fsa_status fsa_validate_frame_sets(int32_t B, int32_t H, int32_t Tq, int32_t Tk,
  *
  * For each batch b, head h in [h_begin, h_end) and query group g (query
  * frames g*q_group .. g*q_group+q_group-1):
- *   qsum[d]   = sum of q over the group's tokens, float64, added one token at
- *               a time in ascending token order;
+ *   qf[t,d]   = sum of q over query frame t's P tokens, float64, added one
+ *               token at a time in ascending order (frame-level compression);
+ *   qsum[d]   = sum of qf over the group's frames, added in frame order;
  *   ksum[f,d] = sum of k over frame f's P tokens, float64, ascending p;
  *   score[f]  = sum over d of (qsum[d]*ksum[f,d]), each product rounded to
  *               float64 then added in ascending d (no fused multiply-add);
@@ -183,8 +184,9 @@ fsa_status fsa_validate_frame_sets(int32_t B, int32_t H, int32_t Tq, int32_t Tk,
  *   out_scores  device [B][H][G][cand_end-cand_begin] float64, or NULL
  *   workspace   device, >= fsa_select_topk_workspace_size() bytes
  * Errors: FSA_E_ARG (topk_k < 1 or > 64, topk_k > number of candidates,
- * candidates outside [0, Tk), q_group does not divide Tq, bad head range),
- * FSA_E_SHAPE, FSA_E_DTYPE, FSA_E_CAPACITY (workspace), FSA_E_HIP.
+ * candidates outside [0, Tk) or more than 4096 of them, q_group does not
+ * divide Tq, bad head range), FSA_E_SHAPE (D outside [1, 256], ...),
+ * FSA_E_DTYPE, FSA_E_CAPACITY (workspace), FSA_E_HIP.
  * Non-finite inputs give unspecified frames (a precondition). */
 fsa_status fsa_select_topk_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t D,
                                           int32_t P, int32_t q_group, int32_t cand_begin,
@@ -215,7 +217,9 @@ fsa_status fsa_select_topk_frames(const void *q, const void *k, int32_t dt, int3
  * its row sums in float32, and forms P.V with float16 MFMA on float16
  * probabilities and float16 values (float32 accumulation); O and LSE are
  * float32.
- * Supported: D in {64, 128}; P >= 1; Nq % P == 0; Nk % P == 0.
+ * Supported: D in {64, 128}; P >= 1; Nq % P == 0; Nk % P == 0.  The bf16
+ * path reads and writes 16 bytes at a time: q, k, v, o and the workspace must
+ * be 16-byte aligned (FSA_E_ARG otherwise).
  * Errors: FSA_E_ARG, FSA_E_SHAPE, FSA_E_DTYPE, FSA_E_CAPACITY, FSA_E_HIP. */
 fsa_status fsa_sparse_frame_attn_workspace_size(int32_t dt, int32_t B, int32_t H, int32_t Nk,
                                                 int32_t D, size_t *bytes);
@@ -246,6 +250,24 @@ fsa_status fsa_sparse_frame_attn_prepared(const void *q, const void *k, const vo
                                           const int32_t *cnt, int32_t cap, float scale,
                                           float *o, float *lse, size_t prepared_bytes,
                                           void *stream);
+
+/* device.  Single-pass decomposable attention [ISPA §2 item 1: the local
+ * stream (current frames + sink) and the full-history stream are both
+ * collected in one forward pass with negligible extra FLOPs, through the LSE
+ * state].  For every query row of frame t, with A = A_a(t) and B = A_b(t)
+ * (two frame lists, disjoint for an exact union):
+ *   (o_a,  lse_a)  = attention over the frames of A            (local branch)
+ *   (o_ab, lse_ab) = attention over the frames of A and B      (full branch)
+ * The kernel walks the runs of A, writes its running state to (o_a, lse_a),
+ * and continues over the runs of B from that same state, so the union costs
+ * one pass over the keys; overlapping lists count shared frames twice.
+ * bf16 only, values from fsa_prepare_values; cap_a + cap_b <= FSA_MAX_CAP.
+ * Shapes, precision, alignment and errors as fsa_sparse_frame_attn_prepared. */
+fsa_status fsa_sparse_frame_attn_dual_prepared(
+    const void *q, const void *k, const void *prepared, int32_t dt, int32_t B, int32_t H,
+    int32_t Nq, int32_t Nk, int32_t D, int32_t P, const int32_t *idx_a, const int32_t *cnt_a,
+    int32_t cap_a, const int32_t *idx_b, const int32_t *cnt_b, int32_t cap_b, float scale,
+    float *o_a, float *lse_a, float *o_ab, float *lse_ab, size_t prepared_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * LSE merge  [ISPA §2 item 1, §3 item 2]

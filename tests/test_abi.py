@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(fsa.EXPORTED)
@@ -63,6 +63,8 @@ def _attn(**kw):
     (dict(ws_bytes=10), 4, "workspace"),
     (dict(ws=None), 1, "workspace is NULL"),
     (dict(scale=float("inf")), 1, "scale"),
+    (dict(q=ctypes.c_void_p(24)), 1, "16-byte aligned"),
+    (dict(ws=ctypes.c_void_p(40)), 1, "16-byte aligned"),
 ])
 def test_attention_argument_errors(kw, status, text):
     assert _attn(**kw) == status
@@ -99,7 +101,7 @@ def test_workspace_size_queries():
     assert lib.fsa_sparse_frame_attn_workspace_size(0, 1, 1, 13, 80, ctypes.byref(n)) == 3
     assert lib.fsa_select_topk_workspace_size(1, 12, 4680, 128, 1560, 3, 0, 57,
                                               ctypes.byref(n)) == 0
-    assert n.value == 1 * 12 * (1 + 57) * 128 * 8
+    assert n.value == 1 * 12 * (3 + 57) * 128 * 8
 
 
 def _topk(**kw):

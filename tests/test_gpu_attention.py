@@ -154,3 +154,56 @@ def test_zero_queries_closed_form():
     lists = [[[[0], [0, 1], [1, 2, 3], [0, 1, 2, 3]]]]
     idx, cnt = _lists_to_arrays(lists, B, H)
     _run_and_check(q, k, v, idx, cnt, P, "bf16", "zero queries")
+
+
+@pytest.mark.parametrize("Nk,D", [(1, 64), (13, 128), (64, 128), (100, 64), (1560, 128)])
+def test_prepare_values_layout(Nk, D):
+    # prepared V = float16, key-chunked transposed [B*H][ceil(Nk/8)][D][8], zero past Nk
+    B, H = 1, 3
+    v = _rand((B, H, Nk, D), torch.bfloat16, 31, outliers=2)
+    _say(f"prepare_values Nk={Nk} D={D}")
+    prep = fsa.prepare_values(v.to(DEV))
+    torch.cuda.synchronize()
+    NkC = -(-Nk // 8)
+    got = prep.view(torch.float16)[:B * H * NkC * D * 8].view(B * H, NkC, D, 8).cpu()
+    ref = torch.zeros(B * H, NkC * 8, D, dtype=torch.float16)
+    ref[:, :Nk] = v.reshape(B * H, Nk, D).to(torch.float16)
+    ref = ref.view(B * H, NkC, 8, D).permute(0, 1, 3, 2)
+    assert torch.equal(got, ref)
+
+
+def test_prepared_path_equals_one_call():
+    w = wl.lvsa_shaped(4).shrunk(H=2, P=136)
+    q, k, v = (t.to(DEV) for t in wl.make_qkv(w))
+    idx, cnt = fsa.build_frame_sets(w.policies[:2], w.B, w.Tq, w.Tk, device=DEV)
+    _say("prepared vs one call")
+    o1, l1 = fsa.sparse_frame_attn(q, k, v, idx, cnt, w.P)
+    prep = fsa.prepare_values(v)
+    o2, l2 = fsa.sparse_frame_attn_prepared(q, k, prep, idx, cnt, w.P)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("D,P", [(64, 40), (128, 150)])
+def test_dual_pass_edges(D, P):
+    # one pass over A then B: O_A = attention over A, O_AB = attention over A ∪ B
+    B, H, T = 1, 2, 5
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s, outliers=2) for s in (41, 42, 43))
+    la = [[[0], [], [1, 3], [], [0, 2, 4]], [[4], [2], [], [0, 1, 2, 3, 4], []]]
+    lb = [[[1, 2], [0, 4], [], [], [1, 3]], [[0, 1], [], [3], [], []]]
+    ia, ca = _lists_to_arrays([la], B, H)
+    ib, cb = _lists_to_arrays([lb], B, H)
+    lu = [[[sorted(a + b) for a, b in zip(la[h], lb[h])] for h in range(H)]]
+    iu, cu = _lists_to_arrays(lu, B, H)
+    prep = fsa.prepare_values(v.to(DEV))
+    _say(f"dual pass D={D} P={P}")
+    oa, la_, oab, lab = fsa.sparse_frame_attn_dual(q.to(DEV), k.to(DEV), prep, ia.to(DEV),
+                                                    ca.to(DEV), ib.to(DEV), cb.to(DEV), P)
+    o1, l1 = fsa.sparse_frame_attn_prepared(q.to(DEV), k.to(DEV), prep, ia.to(DEV), ca.to(DEV), P)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, o1) and torch.equal(la_, l1)   # A's state is the single-list result
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    ra = oatt.sparse_frame_attention(qn, kn, vn, ia.numpy(), ca.numpy(), P)
+    ru = oatt.sparse_frame_attention(qn, kn, vn, iu.numpy(), cu.numpy(), P)
+    assert_close(oa.cpu().numpy(), la_.cpu().numpy(), *ra, "bf16", f"dual O_A D={D}")
+    assert_close(oab.cpu().numpy(), lab.cpu().numpy(), *ru, "bf16", f"dual O_AB D={D}")

@@ -95,6 +95,30 @@ def test_decomposable_branches_merge_to_union():
     assert (om - out["U"][2]).abs().max().item() <= 1e-2
 
 
+def test_decomposable_single_pass_dual_output():
+    # ISPA §2 item 1: local stream (sink + current chunk) and full stream (all 49
+    # frames) from one pass over the keys
+    w = wl.decomposable()
+    q, k, v = wl.make_qkv(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ia, ca = fsa.build_frame_sets(w.branches["A"], w.B, w.Tq, w.Tk, w.offset, w.chunk, device=DEV)
+    ib, cb = fsa.build_frame_sets(w.branches["B"], w.B, w.Tq, w.Tk, w.offset, w.chunk, device=DEV)
+    iu, cu = fsa.build_frame_sets(w.branches["U"], w.B, w.Tq, w.Tk, w.offset, w.chunk, device=DEV)
+    prep = fsa.prepare_values(vd)
+    _say(f"{w.name}: single-pass dual output")
+    oa, la, ou, lu = fsa.sparse_frame_attn_dual(qd, kd, prep, ia, ca, ib, cb, w.P)
+    o_a1, l_a1 = fsa.sparse_frame_attn_prepared(qd, kd, prep, ia, ca, w.P)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, o_a1) and torch.equal(la, l_a1)
+    rows = sample_rows(w.P, range(w.Tq), 48, seed=7)
+    ra = oracle_rows(q, k, v, ia.cpu(), ca.cpu(), w.P, rows)
+    ru = oracle_rows(q, k, v, iu.cpu(), cu.cpu(), w.P, rows)
+    assert_close(oa[:, :, rows].cpu().numpy(), la[:, :, rows].cpu().numpy(), *ra, "bf16",
+                 f"{w.name} dual O_A (local)")
+    assert_close(ou[:, :, rows].cpu().numpy(), lu[:, :, rows].cpu().numpy(), *ru, "bf16",
+                 f"{w.name} dual O_AB (all 49 frames)")
+
+
 @pytest.mark.parametrize("s", [0, 5])
 def test_long_video_sampled_rows(s):
     w = wl.long_video(s)
