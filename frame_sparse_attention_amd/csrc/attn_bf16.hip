@@ -384,8 +384,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ms], acc[db], 0, 0, 0);
         }
       }
-      // the last tile of list A: its state is the attention over A alone
-      if (DUAL && cur.r < nruns_a && nxt.r >= nruns_a) store_out(first);
     }
 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's tile loads have landed in LDS
@@ -396,11 +394,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
     nxt = nn;
   };
   f32x16 sd[2];
-  if (DUAL && wave_active && nruns_a == 0) store_out(first);
+  // DUAL: once the cursor has left the runs of list A, the state holds exactly
+  // the tiles of A (the next tile's S is computed but not yet accumulated)
+  bool a_done = !DUAL;
+  auto after_tile = [&]() {
+    if (DUAL && !a_done && cur.r >= nruns_a) {
+      if (wave_active) store_out(first);
+      a_done = true;
+    }
+  };
+  after_tile();
   while (cur.r < nruns) {
     step(sc, sd);
+    after_tile();
     if (cur.r >= nruns) break;
     step(sd, sc);
+    after_tile();
   }
   if (wave_active) store_out(all);
 }
@@ -446,8 +455,8 @@ fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *p
   auto vt = static_cast<const _Float16 *>(prepared);
   const ListArg la{idx, cnt, cap}, lb{idx_b, cnt_b, cap_b};
   const OutArg first{o_first, lse_first}, all{o, lse};
-  const dim3 grid((unsigned)blocks), block(kThreads);
   const bool dual = idx_b != nullptr;
+  const dim3 grid((unsigned)blocks), block(kThreads);
   if (D == 64) {
     if (dual)
       hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, block, 0, stream, qq, kk, vt, la, lb,
