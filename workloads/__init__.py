@@ -55,6 +55,10 @@ class Workload:
     outlier_scale: float = 8.0
     q_group: int = 1               # query frames pooled together (memory heads)
     branches: dict = field(default_factory=dict)   # extra named policy lists
+    # two-level (frame, then block) selection for the MEMORY heads: tokens per
+    # block and blocks kept per query block; 0 = frame-level lists only
+    block: int = 0
+    topk_blocks: int = 0
 
     @property
     def Nq(self) -> int:
@@ -101,6 +105,18 @@ def ar_chunk() -> Workload:
                     offset=57, chunk=3, q_group=3)
 
 
+def ar_chunk_hsa() -> Workload:
+    """The AR chunk workload (same tensors) with hierarchical selection on the
+    memory heads: per 120-token query block, the 8 best of frames 0..56 by
+    frame-pooled scores, then the 52 best 120-token blocks inside those frames
+    by block-pooled scores, plus the last 3 frames whole.  Lists are in block
+    units (13 blocks per 1560-token frame); heads 0-7 keep their frame windows
+    written in blocks."""
+    w = ar_chunk()
+    return dataclasses.replace(w, name="ar_chunk_hsa_3x1560_cache60_blk120", block=120,
+                               topk_blocks=52)
+
+
 def decomposable() -> Workload:
     """Query chunk 3 x 1560 tokens, KV frames 0 = sink, 1..45 = history, 46..48 =
     current chunk; branch A = current chunk + sink, branch B = history; the merge of
@@ -123,7 +139,8 @@ def long_video(step: int = 0) -> Workload:
                     [dict(pol) for _ in range(24)], steps=8)
 
 
-ALL = {w().name: w for w in (tiny_f32, lvsa_shaped, ar_chunk, decomposable, long_video)}
+ALL = {w().name: w for w in (tiny_f32, lvsa_shaped, ar_chunk, ar_chunk_hsa, decomposable,
+                              long_video)}
 
 
 def _seed(cfg_seed: int, tensor: int, head: int) -> int:
