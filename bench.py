@@ -116,9 +116,10 @@ def time_ms(fn, reps: int = 20) -> float:
 
 
 def aux_rows(dev):
-    """The other hot-path rows at their workload shapes, each against the HBM roof:
-    frame pooling + top-k (AR chunk, memory heads 8-11) and the LSE merge (the
-    decomposable workload's two branches)."""
+    """The other hot-path rows at their workload shapes: frame pooling + top-k
+    (AR chunk, memory heads 8-11) and the LSE merge against the HBM roof; the AR
+    chunk's attention with frame-level and with two-level (frame, then block)
+    memory heads; the decomposable workload's single-pass dual output."""
     import torch
 
     import frame_sparse_attention_amd as fsa
@@ -134,7 +135,48 @@ def aux_rows(dev):
                                  "algorithmic_bytes": nbytes,
                                  "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                  "frac_of_8TBps": round(nbytes / (ms * 1e-3) / 8e12, 4)}
-    del q, k, qd, kd
+    # the AR chunk step: memory-head top-k, lists, attention (values prepared once
+    # per cache, outside the step)
+    v = wl.make_tensor(w, 2).to(dev)
+    prep = fsa.prepare_values(v)
+    cap = fsa.frame_set_capacity(w.policies, w.Tq, w.Tk, w.offset, w.chunk)
+    idx, cnt = fsa.build_frame_sets(w.policies, w.B, w.Tq, w.Tk, w.offset, w.chunk, sel, cap, dev)
+    ms_attn = time_ms(lambda: fsa.sparse_frame_attn_prepared(qd, kd, prep, idx, cnt, w.P))
+
+    def ar_step():
+        fsa.select_topk_frames(qd, kd, w.P, 8, 12, 3, 0, 57, 8, out=sel)
+        i, c = fsa.build_frame_sets(w.policies, w.B, w.Tq, w.Tk, w.offset, w.chunk, sel, cap,
+                                    dev)
+        fsa.sparse_frame_attn_prepared(qd, kd, prep, i, c, w.P)
+
+    ms_step = time_ms(ar_step)
+    pairs = int(cnt.to(torch.int64).sum()) * w.P * w.P
+    out["ar_chunk_attention"] = {
+        "workload": w.name, "ms_attention": round(ms_attn, 4), "ms_step": round(ms_step, 4),
+        "attended_pairs": pairs,
+        "effective_TFLOP_per_s": round(4 * w.D * pairs / (ms_attn * 1e-3) / 1e12, 1)}
+    # the same chunk with two-level (frame, then block) selection on the memory heads
+    hw = wl.ar_chunk_hsa()
+    nb = hw.P // hw.block
+    bpol = wl.block_policies(hw)
+    Tqb, Tkb, ob, cb = hw.Tq * nb, hw.Tk * nb, hw.offset * nb, hw.chunk * nb
+    hcap = max(fsa.frame_set_capacity(bpol, Tqb, Tkb, ob, cb), hw.topk_blocks + 3 * nb)
+    hidx, hcnt = fsa.build_frame_sets(bpol, hw.B, Tqb, Tkb, ob, cb, None, hcap, dev)
+    fsa.select_hsa_blocks(qd, kd, hw.P, hw.block, 8, 12, 3, 8, hw.topk_blocks, hw.offset,
+                          hw.chunk, idx=hidx, cnt=hcnt)
+    ms_sel = time_ms(lambda: fsa.select_hsa_blocks(qd, kd, hw.P, hw.block, 8, 12, 3, 8,
+                                                   hw.topk_blocks, hw.offset, hw.chunk,
+                                                   idx=hidx, cnt=hcnt))
+    ms_hattn = time_ms(lambda: fsa.sparse_frame_attn_prepared(qd, kd, prep, hidx, hcnt,
+                                                              hw.block))
+    hpairs = int(hcnt.to(torch.int64).sum()) * hw.block * hw.block
+    nbytes = 4 * (hw.Nq + 57 * hw.P) * hw.D * 2
+    out["hsa"] = {
+        "workload": hw.name, "ms_select": round(ms_sel, 4), "ms_attention": round(ms_hattn, 4),
+        "select_GB_per_s": round(nbytes / (ms_sel * 1e-3) / 1e9, 1),
+        "attended_pairs": hpairs,
+        "effective_TFLOP_per_s": round(4 * hw.D * hpairs / (ms_hattn * 1e-3) / 1e12, 1)}
+    del q, k, qd, kd, v, prep, idx, cnt, hidx, hcnt
     d = wl.decomposable()
     rows = d.B * d.H * d.Nq
     g = torch.Generator(device="cpu").manual_seed(4)

@@ -70,6 +70,11 @@ _SIGS = {
                                               _psz]),
     "fsa_select_topk_frames": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "fsa_select_hsa_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _i32, _i32, _psz]),
+    "fsa_select_hsa_blocks": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                     _vp, _sz, _vp]),
     "fsa_sparse_frame_attn_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _psz]),
     "fsa_sparse_frame_attn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
@@ -241,6 +246,45 @@ def select_topk_frames(q: torch.Tensor, k: torch.Tensor, P: int, h_begin: int, h
                                        _ptr(out), _ptr(scores), _ptr(ws), nbytes.value,
                                        _stream(q.device)))
     return (out, scores) if return_scores else out
+
+
+def select_hsa_blocks(q: torch.Tensor, k: torch.Tensor, P: int, block: int, h_begin: int,
+                      h_end: int, n_recent: int, topk_frames: int, topk_blocks: int,
+                      offset: int = 0, chunk: int = 1, cap: int | None = None,
+                      idx: torch.Tensor | None = None, cnt: torch.Tensor | None = None):
+    """Two-level (frame, then block) selection for heads [h_begin, h_end).
+
+    Writes block-unit lists (block index = frame * (P // block) + block in
+    frame) into idx [B, H, Nq // block, cap] and cnt [B, H, Nq // block]
+    (allocated with -1 / 0 when not given; rows of other heads are left as
+    they are) and returns (idx, cnt).  Attend with P = block."""
+    _need_contig(q, k)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if block <= 0:
+        raise ValueError("block must be positive")
+    nb = P // block if P % block == 0 else 0
+    if cap is None:
+        cap = topk_blocks + n_recent * nb if idx is None else idx.shape[3]
+    G = Nq // block
+    if idx is None:
+        idx = torch.full((B, H, G, cap), -1, dtype=torch.int32, device=q.device)
+    if cnt is None:
+        cnt = torch.zeros((B, H, G), dtype=torch.int32, device=q.device)
+    _need_contig(idx, cnt)
+    if idx.dtype != torch.int32 or cnt.dtype != torch.int32:
+        raise TypeError("idx and cnt must be int32")
+    if idx.shape != (B, H, G, cap) or cnt.shape != (B, H, G):
+        raise ValueError("idx must be [B, H, Nq // block, cap] and cnt [B, H, Nq // block]")
+    nbytes = ctypes.c_size_t(0)
+    _check(_load().fsa_select_hsa_workspace_size(B, H, Nq, Nk, D, P, block, offset, chunk,
+                                              h_begin, h_end, n_recent, ctypes.byref(nbytes)))
+    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)
+    _check(_load().fsa_select_hsa_blocks(_ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P,
+                                      block, offset, chunk, h_begin, h_end, n_recent,
+                                      topk_frames, topk_blocks, cap, _ptr(idx), _ptr(cnt),
+                                      _ptr(ws), nbytes.value, _stream(q.device)))
+    return idx, cnt
 
 
 # ----------------------------------------------------------------------------- attention

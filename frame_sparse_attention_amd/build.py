@@ -27,6 +27,7 @@ SOURCES = [
     "frame_sets.hip",
     "merge.hip",
     "topk.hip",
+    "hsa.hip",
     "attn_f32.hip",
     "attn_bf16.hip",
 ]

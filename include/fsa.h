@@ -199,6 +199,54 @@ fsa_status fsa_select_topk_frames(const void *q, const void *k, int32_t dt, int3
                                   size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Two-level (frame, then block) selection  [LF §2.2 hierarchical sparse
+ * attention: token compression to block and frame granularity, frame
+ * selection per query block with frame-level keys, block selection inside the
+ * chosen frames with block-level keys; Head Forcing methodology §2 for the
+ * recent frames kept whole]
+ *
+ * device.  Writes block-unit lists for heads [h_begin, h_end): a block is
+ * `block` consecutive tokens of a frame (P % block == 0, nb = P / block), and
+ * block index g = frame * nb + block-in-frame.  For query block j (tokens
+ * [j*block, (j+1)*block), query frame tq = j / nb, whose chunk ends at KV
+ * frame e = q_kv_offset + (tq / chunk + 1) * chunk - 1):
+ *   qs      = sum of the block's query tokens (float64, ascending tokens)
+ *   kblk[g] = sum of key block g's tokens (float64, ascending tokens)
+ *   kfr[f]  = sum of frame f's nb block sums (float64, ascending blocks)
+ *   level 1: the topk_frames best frames f in [0, e - n_recent] by
+ *            qs . kfr[f] (rounded products added in ascending channel order),
+ *            ties to the lower frame
+ *   level 2: the topk_blocks best blocks of those frames by qs . kblk[g],
+ *            ties to the lower block
+ *   idx row = the chosen blocks ascending, then every block of the frames
+ *            e - n_recent + 1 .. e ascending; cnt = topk_blocks + n_recent*nb;
+ *            the rest of the row is -1.
+ * Rows of heads outside [h_begin, h_end) are not touched, so other heads'
+ * block-unit lists can come from fsa_build_frame_sets with every frame size
+ * and count multiplied by nb.  Attend with P = block.
+ *   q, k        device [B][H][Nq][D] / [B][H][Nk][D], float32 or bfloat16
+ *   idx, cnt    device int32 [B][H][Nq/block][cap] / [B][H][Nq/block] out
+ *   workspace   device, >= fsa_select_hsa_workspace_size() bytes
+ * Errors: FSA_E_ARG (bad head range; the last chunk ends past the cache;
+ * recent frames before frame 0; topk_frames outside [1, candidates of the
+ * first chunk]; topk_frames * nb > 4096; topk_blocks outside
+ * [0, topk_frames * nb]; more than 4096 candidate frames), FSA_E_SHAPE (D
+ * outside [1, 256]; P not a multiple of block; Nq or Nk not a multiple of P),
+ * FSA_E_DTYPE, FSA_E_CAPACITY (cap below topk_blocks + n_recent*nb or above
+ * FSA_MAX_CAP; workspace), FSA_E_HIP.  Non-finite inputs give unspecified
+ * blocks (a precondition). */
+fsa_status fsa_select_hsa_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t Nk, int32_t D,
+                                         int32_t P, int32_t block, int32_t q_kv_offset,
+                                         int32_t chunk, int32_t h_begin, int32_t h_end,
+                                         int32_t n_recent, size_t *bytes);
+fsa_status fsa_select_hsa_blocks(const void *q, const void *k, int32_t dt, int32_t B, int32_t H,
+                                 int32_t Nq, int32_t Nk, int32_t D, int32_t P, int32_t block,
+                                 int32_t q_kv_offset, int32_t chunk, int32_t h_begin,
+                                 int32_t h_end, int32_t n_recent, int32_t topk_frames,
+                                 int32_t topk_blocks, int32_t cap, int32_t *idx, int32_t *cnt,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Sparse frame attention  [LVSA §2 core mechanism and complexity; LF §2.2
  * execution over the selected frames; ISPA §2 item 1 (LSE output)]
  *

@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(fsa.EXPORTED)
@@ -168,3 +168,52 @@ def test_build_module_imports_without_the_library():
     import importlib
     mod = importlib.import_module("frame_sparse_attention_amd.build")
     assert mod.ARCH == "gfx950" and "attn_bf16.hip" in mod.SOURCES
+
+
+def _hsa(**kw):
+    # the AR chunk with block-level memory heads: 3 query frames of 1560 tokens,
+    # a 60-frame cache, blocks of 120 tokens (13 per frame)
+    a = dict(q=BAD, k=BAD, dt=1, B=1, H=12, Nq=4680, Nk=93600, D=128, P=1560, block=120,
+             offset=57, chunk=3, h_begin=8, h_end=12, n_recent=3, kf=8, kb=52, cap=91,
+             idx=BAD, cnt=BAD, ws=BAD, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.fsa_select_hsa_blocks(a["q"], a["k"], a["dt"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                     a["D"], a["P"], a["block"], a["offset"], a["chunk"],
+                                     a["h_begin"], a["h_end"], a["n_recent"], a["kf"], a["kb"],
+                                     a["cap"], a["idx"], a["cnt"], a["ws"], a["ws_bytes"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(dt=5), 3, "dtype"),
+    (dict(D=300), 2, "D=300"),
+    (dict(block=7), 2, "multiple of block"),
+    (dict(Nq=4000), 2, "Nq=4000"),
+    (dict(chunk=0), 1, "chunk=0"),
+    (dict(offset=58), 1, "beyond"),
+    (dict(n_recent=61), 1, "before KV frame 0"),
+    (dict(n_recent=-1), 1, "n_recent=-1"),
+    (dict(h_begin=9, h_end=8), 1, "head range"),
+    (dict(kf=0), 1, "topk_frames=0"),
+    (dict(kf=58), 1, "topk_frames=58"),
+    (dict(kb=105), 1, "topk_blocks=105"),
+    (dict(kb=-1), 1, "topk_blocks=-1"),
+    (dict(cap=90), 4, "cap=90"),
+    (dict(cap=2000, kb=52), 4, "cap=2000"),
+    (dict(q=None), 1, "null"),
+    (dict(ws_bytes=1000), 4, "workspace"),
+])
+def test_select_hsa_argument_checks(kw, status, text):
+    assert _hsa(**kw) == status
+    assert text in fsa.last_error()
+
+
+def test_select_hsa_workspace_size_and_empty_calls():
+    n = ctypes.c_size_t(0)
+    assert lib.fsa_select_hsa_workspace_size(1, 12, 4680, 93600, 128, 1560, 120, 57, 3, 8, 12,
+                                             3, ctypes.byref(n)) == 0
+    # 4 heads x (39 query blocks + 57*13 key blocks + 57 frames) x 128 doubles
+    assert n.value == 4 * (39 + 57 * 13 + 57) * 128 * 8
+    # nothing to do: no heads, or no batch
+    assert _hsa(h_begin=8, h_end=8) == 0
+    assert _hsa(B=0) == 0

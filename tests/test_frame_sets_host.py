@@ -92,3 +92,28 @@ def test_validator_flags_bad_lists():
         with pytest.raises(fsa.FsaError, match=msg):
             fsa.validate_frame_sets(i, c, 5)
     fsa.validate_frame_sets(idx[:, :, :1], cnt[:, :, :1], 5)
+
+
+@pytest.mark.parametrize("make", [wl.ar_chunk_hsa])
+def test_block_unit_frame_windows_match_oracle(make):
+    # the frame windows of the non-memory heads, written in block units, from the
+    # library's builder against the oracle's own scaling of the same policies
+    from oracle import hsa as ohsa
+    w = make()
+    nb = w.P // w.block
+    bpol = wl.block_policies(w)
+    Tqb, Tkb, ob, cb = w.Tq * nb, w.Tk * nb, w.offset * nb, w.chunk * nb
+    cap = fsa.frame_set_capacity(bpol, Tqb, Tkb, ob, cb)
+    idx, cnt = fsa.build_frame_sets_host(bpol, w.B, Tqb, Tkb, ob, cb, None, cap)
+    for h, p in enumerate(w.policies):
+        if p["kind"] == wl.MEMORY:
+            continue
+        oidx, ocnt = ofs.build([ohsa.scale_policy_to_blocks(p, nb)], w.B, Tqb, Tkb, ob, cb,
+                               cap=cap)
+        np.testing.assert_array_equal(idx[:, h:h + 1], oidx)
+        np.testing.assert_array_equal(cnt[:, h:h + 1], ocnt)
+        # and every query block sees whole frames: the frame list times nb
+        fidx, fcnt = ofs.build([p], w.B, w.Tq, w.Tk, w.offset, w.chunk)
+        frames = fidx[0, 0, 0, :fcnt[0, 0, 0]]
+        assert idx[0, h, 0, :cnt[0, h, 0]].tolist() == [f * nb + i for f in frames
+                                                        for i in range(nb)]

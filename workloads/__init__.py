@@ -117,6 +117,27 @@ def ar_chunk_hsa() -> Workload:
                                topk_blocks=52)
 
 
+def block_policies(w: Workload) -> list:
+    """The heads' policies in block units for a workload with `block` set: every
+    frame count of a SINK_WINDOW / RANGE head is multiplied by the blocks per
+    frame; a MEMORY head gets a window over its recent frames as a placeholder
+    (its rows are written by the two-level selection)."""
+    nb = w.P // w.block
+    out = []
+    for p in w.policies:
+        p = dict(p)
+        if p["kind"] == SINK_WINDOW:
+            p.update(n_sink=p["n_sink"] * nb, window=p["window"] * nb)
+        elif p["kind"] == RANGE:
+            p.update(lo=p["lo"] * nb, hi=p["hi"] * nb + nb - 1)
+        elif p["kind"] == MEMORY:
+            p = policy(SINK_WINDOW, n_sink=0, window=p["n_recent"] * nb)
+        elif p["kind"] != FULL:
+            raise ValueError("policy kind has no block-unit form")
+        out.append(p)
+    return out
+
+
 def decomposable() -> Workload:
     """Query chunk 3 x 1560 tokens, KV frames 0 = sink, 1..45 = history, 46..48 =
     current chunk; branch A = current chunk + sink, branch B = history; the merge of
