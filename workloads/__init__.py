@@ -59,6 +59,10 @@ class Workload:
     # block and blocks kept per query block; 0 = frame-level lists only
     block: int = 0
     topk_blocks: int = 0
+    # per-head frame-level rotary re-encoding of the assembled cache: rotated
+    # leading channels (0 = none) and the frequency base
+    rope_dims: int = 0
+    rope_base: float = 10000.0
 
     @property
     def Nq(self) -> int:
@@ -117,6 +121,15 @@ def ar_chunk_hsa() -> Workload:
                                topk_blocks=52)
 
 
+def ar_chunk_rope() -> Workload:
+    """The AR chunk workload (same tensors and frame sets) with each head's
+    assembled cache re-encoded: the first 42 of 128 channels (a third of the
+    pairs, the temporal part) turn by the frame's rank in the head's set,
+    frequencies 10000^(-2i/42)."""
+    w = ar_chunk()
+    return dataclasses.replace(w, name="ar_chunk_rope_3x1560_cache60_rot42", rope_dims=42)
+
+
 def block_policies(w: Workload) -> list:
     """The heads' policies in block units for a workload with `block` set: every
     frame count of a SINK_WINDOW / RANGE head is multiplied by the blocks per
@@ -160,8 +173,8 @@ def long_video(step: int = 0) -> Workload:
                     [dict(pol) for _ in range(24)], steps=8)
 
 
-ALL = {w().name: w for w in (tiny_f32, lvsa_shaped, ar_chunk, ar_chunk_hsa, decomposable,
-                              long_video)}
+ALL = {w().name: w for w in (tiny_f32, lvsa_shaped, ar_chunk, ar_chunk_hsa, ar_chunk_rope,
+                              decomposable, long_video)}
 
 
 def _seed(cfg_seed: int, tensor: int, head: int) -> int:
