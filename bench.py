@@ -119,7 +119,8 @@ def aux_rows(dev):
     """The other hot-path rows at their workload shapes: frame pooling + top-k
     (AR chunk, memory heads 8-11) and the LSE merge against the HBM roof; the AR
     chunk's attention with frame-level and with two-level (frame, then block)
-    memory heads; the decomposable workload's single-pass dual output."""
+    memory heads, and its per-head rotary re-encoding (HBM roof); the
+    decomposable workload's single-pass dual output."""
     import torch
 
     import frame_sparse_attention_amd as fsa
@@ -155,6 +156,20 @@ def aux_rows(dev):
         "workload": w.name, "ms_attention": round(ms_attn, 4), "ms_step": round(ms_step, 4),
         "attended_pairs": pairs,
         "effective_TFLOP_per_s": round(4 * w.D * pairs / (ms_attn * 1e-3) / 1e12, 1)}
+    # per-head frame-level rotary re-encoding of the assembled cache (one frame
+    # set per head: the chunk's), then attention on the re-encoded Q and K
+    rw = wl.ar_chunk_rope()
+    idx_h, cnt_h = idx[:, :, 0].contiguous(), cnt[:, :, 0].contiguous()
+    qo, ko = fsa.rope_reencode(qd, kd, idx_h, cnt_h, rw.P, rw.rope_dims, rw.rope_base, rw.offset)
+    ms_rope = time_ms(lambda: fsa.rope_reencode(qd, kd, idx_h, cnt_h, rw.P, rw.rope_dims,
+                                                rw.rope_base, rw.offset, q_out=qo, k_out=ko))
+    listed_frames = int(cnt_h.to(torch.int64).sum())
+    nbytes = 2 * 2 * rw.D * (rw.B * rw.H * rw.Nq + listed_frames * rw.P)   # read + write, bf16
+    out["rope_reencode"] = {"workload": rw.name, "ms": round(ms_rope, 4),
+                            "algorithmic_bytes": nbytes,
+                            "GB_per_s": round(nbytes / (ms_rope * 1e-3) / 1e9, 1),
+                            "frac_of_8TBps": round(nbytes / (ms_rope * 1e-3) / 8e12, 4)}
+    del qo, ko
     # the same chunk with two-level (frame, then block) selection on the memory heads
     hw = wl.ar_chunk_hsa()
     nb = hw.P // hw.block

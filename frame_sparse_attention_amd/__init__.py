@@ -75,6 +75,8 @@ _SIGS = {
     "fsa_select_hsa_blocks": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                      _vp, _sz, _vp]),
+    "fsa_rope_reencode": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                 _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
     "fsa_sparse_frame_attn_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _psz]),
     "fsa_sparse_frame_attn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
@@ -285,6 +287,33 @@ def select_hsa_blocks(q: torch.Tensor, k: torch.Tensor, P: int, block: int, h_be
                                       topk_frames, topk_blocks, cap, _ptr(idx), _ptr(cnt),
                                       _ptr(ws), nbytes.value, _stream(q.device)))
     return idx, cnt
+
+
+def rope_reencode(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, cnt: torch.Tensor,
+                  P: int, rot: int, base: float = 10000.0, offset: int = 0,
+                  q_out: torch.Tensor | None = None, k_out: torch.Tensor | None = None):
+    """Per-head frame-level rotary re-encoding for one frame set per (b, h):
+    idx int32 [B, H, cap], cnt int32 [B, H].  Returns (q_out, k_out); q_out has
+    every row written, k_out only the rows of listed frames (a fresh k_out
+    starts as a copy of k).  Either output may be its input (in place)."""
+    _need_contig(q, k, idx, cnt)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, D) or k.dtype != q.dtype:
+        raise ValueError("k must be [B, H, Nk, D] with q's dtype")
+    if idx.dtype != torch.int32 or cnt.dtype != torch.int32:
+        raise TypeError("idx and cnt must be int32")
+    if idx.dim() != 3 or idx.shape[:2] != (B, H) or cnt.shape != (B, H):
+        raise ValueError("idx must be [B, H, cap] and cnt [B, H]")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = k.clone()
+    _need_contig(q_out, k_out)
+    _check(_load().fsa_rope_reencode(_ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P,
+                                  _ptr(idx), _ptr(cnt), idx.shape[2], offset, rot, float(base),
+                                  _ptr(q_out), _ptr(k_out), _stream(q.device)))
+    return q_out, k_out
 
 
 # ----------------------------------------------------------------------------- attention

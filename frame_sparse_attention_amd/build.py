@@ -28,6 +28,7 @@ SOURCES = [
     "merge.hip",
     "topk.hip",
     "hsa.hip",
+    "rope.hip",
     "attn_f32.hip",
     "attn_bf16.hip",
 ]

@@ -38,13 +38,15 @@
  *           §2 core mechanism (A(t) = G ∪ W(t), rotating anchors, widened
  *           window, budget C) and its complexity paragraph.
  *  [LF]     Light Forcing: §2.2 hierarchical sparse attention (mean-pooled
- *           queries/keys, frame selection per query block, attention over
- *           the selected frames only).
+ *           queries/keys, frame selection per query block, block selection
+ *           inside the chosen frames, attention over the selected pairs
+ *           only).
  *  [ISPA]   ISPA, instance-specific parametric absorption: §2 item 1
  *           dual-stream warmup and decomposable attention merged through LSE;
  *           §3 item 2.
  *  [HF]     Head Forcing: methodology §2, per-head KV sets (local, anchor,
- *           memory with fast memory of recent frames).
+ *           memory with fast memory of recent frames); §3 per-head RoPE
+ *           re-encoding of the assembled cache.
  *  [ARL2]   ARL2: §2.1 item 1, bidirectional softmax inside each frame
  *           (the special case A(t) = {t}).
  */
@@ -245,6 +247,35 @@ fsa_status fsa_select_hsa_blocks(const void *q, const void *k, int32_t dt, int32
                                  int32_t h_end, int32_t n_recent, int32_t topk_frames,
                                  int32_t topk_blocks, int32_t cap, int32_t *idx, int32_t *cnt,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Per-head frame-level RoPE re-encoding  [HF §3: keys cached with the spatial
+ * rotary encoding only; frame-level positions encoded again per head when
+ * its cache is assembled, keeping query-key relative positions in range]
+ *
+ * device.  For each (b, h) with its sorted, duplicate-free frame set
+ * A = idx[b][h][0..cnt[b][h]) (frames outside [0, Tk) are skipped):
+ *   key rows of frame A[r]            turn by position r
+ *   query rows of query frame tq      turn by #{f in A : f < q_kv_offset + tq}
+ * Turning by position p: channel pair (2i, 2i+1), i < rot/2, becomes
+ *   (x0 c - x1 s, x0 s + x1 c),  c, s = cos, sin(p * base^(-2i/rot)),
+ * in float64 without fused multiply-add, rounded once to the storage type
+ * (nearest, ties to even); channels >= rot are copied unchanged.
+ *   q, k          device [B][H][Nq][D] / [B][H][Nk][D] (dt: FSA_F32/FSA_BF16)
+ *   idx, cnt      device int32 [B][H][cap] / [B][H]: one frame set per head
+ *                 (e.g. the set shared by a chunk's query frames)
+ *   q_out         device [B][H][Nq][D]: every row written (may alias q)
+ *   k_out         device [B][H][Nk][D]: only rows of listed frames written
+ *                 (may alias k); attend to k_out with the same set
+ * Requires 16-byte aligned q, k, q_out, k_out.
+ * Errors: FSA_E_ARG (rot odd or outside [0, D]; base not positive and
+ * finite; negative offset; null or misaligned pointer), FSA_E_SHAPE (D not a
+ * multiple of 8 in [8, 256]; Nq or Nk not a multiple of P), FSA_E_DTYPE,
+ * FSA_E_CAPACITY (cap outside [1, FSA_MAX_CAP]), FSA_E_HIP. */
+fsa_status fsa_rope_reencode(const void *q, const void *k, int32_t dt, int32_t B, int32_t H,
+                             int32_t Nq, int32_t Nk, int32_t D, int32_t P, const int32_t *idx,
+                             const int32_t *cnt, int32_t cap, int32_t q_kv_offset, int32_t rot,
+                             double base, void *q_out, void *k_out, void *stream);
 
 /* ------------------------------------------------------------------------
  * Sparse frame attention  [LVSA §2 core mechanism and complexity; LF §2.2

@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(fsa.EXPORTED)
@@ -217,3 +217,37 @@ def test_select_hsa_workspace_size_and_empty_calls():
     # nothing to do: no heads, or no batch
     assert _hsa(h_begin=8, h_end=8) == 0
     assert _hsa(B=0) == 0
+
+
+def _rope(**kw):
+    a = dict(q=BAD, k=BAD, dt=1, B=1, H=12, Nq=4680, Nk=93600, D=128, P=1560, idx=BAD, cnt=BAD,
+             cap=11, offset=57, rot=42, base=10000.0, qo=BAD, ko=BAD, stream=None)
+    a.update(kw)
+    return lib.fsa_rope_reencode(a["q"], a["k"], a["dt"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                 a["D"], a["P"], a["idx"], a["cnt"], a["cap"], a["offset"],
+                                 a["rot"], a["base"], a["qo"], a["ko"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(dt=2), 3, "dtype"),
+    (dict(D=100), 2, "D=100"),
+    (dict(D=264), 2, "D=264"),
+    (dict(P=0), 2, "P=0"),
+    (dict(Nk=93601), 2, "Nk=93601"),
+    (dict(rot=43), 1, "rot=43"),
+    (dict(rot=130), 1, "rot=130"),
+    (dict(base=0.0), 1, "base"),
+    (dict(base=float("inf")), 1, "base"),
+    (dict(cap=0), 4, "cap=0"),
+    (dict(offset=-1), 1, "q_kv_offset=-1"),
+    (dict(ko=None), 1, "null"),
+    (dict(qo=ctypes.c_void_p(24)), 1, "aligned"),
+    (dict(H=-1), 1, "negative"),
+])
+def test_rope_argument_checks(kw, status, text):
+    assert _rope(**kw) == status
+    assert text in fsa.last_error()
+
+
+def test_rope_nothing_to_do():
+    assert _rope(B=0) == 0 and _rope(H=0) == 0
