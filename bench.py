@@ -192,6 +192,18 @@ def aux_rows(dev):
         "attended_pairs": hpairs,
         "effective_TFLOP_per_s": round(4 * hw.D * hpairs / (ms_hattn * 1e-3) / 1e12, 1)}
     del q, k, qd, kd, v, prep, idx, cnt, hidx, hcnt
+    # chunk-aware growth schedule of a 60-chunk rollout (host code: a schedule
+    # step before each chunk's list building)
+    import time as _time
+    n_chunks = 60
+    cost = [3.0 * 3 * (i + 1) for i in range(n_chunks)]
+    cand = [max(1, 3 * i) for i in range(n_chunks)]
+    reps = 200
+    t0 = _time.perf_counter()
+    for _ in range(reps):
+        fsa.cag_schedule(cost, 0.6, 0.9, 0.95, cand)
+    out["cag_schedule"] = {"chunks": n_chunks,
+                           "us_host": round((_time.perf_counter() - t0) / reps * 1e6, 2)}
     d = wl.decomposable()
     rows = d.B * d.H * d.Nq
     g = torch.Generator(device="cpu").manual_seed(4)

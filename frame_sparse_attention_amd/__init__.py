@@ -75,6 +75,8 @@ _SIGS = {
     "fsa_select_hsa_blocks": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                      _vp, _sz, _vp]),
+    "fsa_cag_schedule": (_i32, [_i32, _vp, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                _vp, _vp, _vp, _vp]),
     "fsa_rope_reencode": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                  _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
     "fsa_sparse_frame_attn_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _psz]),
@@ -287,6 +289,26 @@ def select_hsa_blocks(q: torch.Tensor, k: torch.Tensor, P: int, block: int, h_be
                                       topk_frames, topk_blocks, cap, _ptr(idx), _ptr(cnt),
                                       _ptr(ws), nbytes.value, _stream(q.device)))
     return idx, cnt
+
+
+def cag_schedule(cost, s_target: float, s_base: float, s_max: float, candidates=None):
+    """Per-chunk sparsity s_i (chunk 0 dense, later chunks sparser) matching the
+    total cost to a target sparsity; returns (sparsity float64 array, budgets
+    int32 array or None, beta).  Host only."""
+    cost = np.ascontiguousarray(cost, dtype=np.float64)
+    n = cost.shape[0]
+    sp = np.empty(n, dtype=np.float64)
+    bud = None
+    cand = None
+    if candidates is not None:
+        cand = np.ascontiguousarray(candidates, dtype=np.int32)
+        if cand.shape != (n,):
+            raise ValueError("candidates must have one entry per chunk")
+        bud = np.empty(n, dtype=np.int32)
+    beta = ctypes.c_double(0.0)
+    _check(_load().fsa_cag_schedule(n, _ptr(cost), float(s_target), float(s_base), float(s_max),
+                                 _ptr(cand), _ptr(sp), _ptr(bud), ctypes.byref(beta)))
+    return sp, bud, beta.value
 
 
 def rope_reencode(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, cnt: torch.Tensor,

@@ -24,6 +24,7 @@ LIB = os.path.join(PKG, "libfsa.so")
 SOURCES = [
     "errors.cpp",
     "attn_api.cpp",
+    "cag.cpp",
     "frame_sets.hip",
     "merge.hip",
     "topk.hip",

@@ -37,7 +37,8 @@
  *  [LVSA]   LVSA, training-free sparse attention for long video diffusion:
  *           §2 core mechanism (A(t) = G ∪ W(t), rotating anchors, widened
  *           window, budget C) and its complexity paragraph.
- *  [LF]     Light Forcing: §2.2 hierarchical sparse attention (mean-pooled
+ *  [LF]     Light Forcing: §2.1 chunk-aware growth of the sparsity ratio;
+ *           §2.2 hierarchical sparse attention (mean-pooled
  *           queries/keys, frame selection per query block, block selection
  *           inside the chosen frames, attention over the selected pairs
  *           only).
@@ -199,6 +200,31 @@ fsa_status fsa_select_topk_frames(const void *q, const void *k, int32_t dt, int3
                                   int32_t cand_begin, int32_t cand_end, int32_t topk_k,
                                   int32_t *out_frames, double *out_scores, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Chunk-aware growth of the sparsity ratio  [LF §2.1: first chunk dense,
+ * later chunks sparser, s_i = s_base - alpha_i * beta with alpha_i following
+ * the noise level as 1/sqrt, beta matching the total FLOPs to a target]
+ *
+ * host, synchronous.  For chunks i = 0..n_chunks-1 with dense attention cost
+ * cost[i] > 0:
+ *   s_0 = 0;  s_i = clip(s_base - beta / sqrt(i + 1), 0, s_max)  (i >= 1)
+ *   beta: the upper end of a fixed float64 bisection (at most 200 halvings)
+ *         of a bracket clipping every s_i at s_max at one end and at 0 at the
+ *         other, with sum_i (1 - s_i) cost[i] >= (1 - s_target) sum_i cost[i]
+ *         (sums in ascending i, no fused multiply-add)
+ *   budgets[i] = floor((1 - s_i) * candidates[i] + 1/2) clipped to
+ *         [1, candidates[i]]: frames (or blocks) kept by chunk i
+ *   sparsity    host double [n_chunks] out
+ *   candidates  host int32 [n_chunks], needed only with budgets
+ *   budgets     host int32 [n_chunks] out, or NULL
+ *   beta_out    host double out, or NULL
+ * Errors: FSA_E_ARG (n_chunks < 1; null pointer; s_target or s_max outside
+ * [0, 1), s_base outside [0, 1]; a cost not positive and finite; a
+ * candidate count < 1; a target that no beta reaches). */
+fsa_status fsa_cag_schedule(int32_t n_chunks, const double *cost, double s_target, double s_base,
+                            double s_max, const int32_t *candidates, double *sparsity,
+                            int32_t *budgets, double *beta_out);
 
 /* ------------------------------------------------------------------------
  * Two-level (frame, then block) selection  [LF §2.2 hierarchical sparse
