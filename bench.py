@@ -192,6 +192,25 @@ def aux_rows(dev):
         "attended_pairs": hpairs,
         "effective_TFLOP_per_s": round(4 * hw.D * hpairs / (ms_hattn * 1e-3) / 1e12, 1)}
     del q, k, qd, kd, v, prep, idx, cnt, hidx, hcnt
+    # the long-video workload (H24, 126 frames x 3600 tokens, C33 W11 T_per8), one
+    # step: inputs drawn on the device (same shape and distribution; the seeded
+    # CPU recipe of the parity tests would take minutes at this size)
+    lv = wl.long_video()
+    gen = torch.Generator(device=dev).manual_seed(lv.seed)
+    qv, kv_, vv = (torch.randn((lv.B, lv.H, lv.Nq, lv.D), generator=gen, device=dev,
+                               dtype=torch.float32).to(torch.bfloat16) for _ in range(3))
+    lidx, lcnt = fsa.build_frame_sets(lv.policies, lv.B, lv.Tq, lv.Tk, device=dev)
+    lprep = fsa.prepare_values(vv)
+    lo_, ll_ = fsa.sparse_frame_attn_prepared(qv, kv_, lprep, lidx, lcnt, lv.P)
+    ms_lv = time_ms(lambda: fsa.sparse_frame_attn_prepared(qv, kv_, lprep, lidx, lcnt, lv.P,
+                                                           out=lo_, out_lse=ll_), 3)
+    lpairs = int(lcnt.to(torch.int64).sum()) * lv.P * lv.P
+    out["long_video_step"] = {
+        "workload": lv.name, "ms_attention": round(ms_lv, 2), "attended_pairs": lpairs,
+        "effective_TFLOP_per_s": round(4 * lv.D * lpairs / (ms_lv * 1e-3) / 1e12, 1),
+        "pct_bf16_peak": round(100 * 4 * lv.D * lpairs / (ms_lv * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del qv, kv_, vv, lprep, lo_, ll_, lidx, lcnt
+    torch.cuda.empty_cache()
     # chunk-aware growth schedule of a 60-chunk rollout (host code: a schedule
     # step before each chunk's list building)
     import time as _time

@@ -85,6 +85,10 @@ _SIGS = {
     "fsa_prepare_values": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "fsa_sparse_frame_attn_prepared": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _i32, _vp, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
+    "fsa_attn_split_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _pi32, _psz]),
+    "fsa_sparse_frame_attn_prepared_split": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                    _i32, _i32, _vp, _vp, _i32, _f32, _i32, _vp,
+                                                    _vp, _sz, _vp, _sz, _vp]),
     "fsa_sparse_frame_attn_dual_prepared": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                                    _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32,
                                                    _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -411,6 +415,45 @@ def sparse_frame_attn_prepared(q: torch.Tensor, k: torch.Tensor, prepared: torch
         _ptr(q), _ptr(k), _ptr(prepared), _dtype_code(q), B, H, Nq, Nk, D, P, _ptr(idx),
         _ptr(cnt), idx.shape[3], float(scale) if scale is not None else 0.0, _ptr(o), _ptr(lse),
         prepared.numel() * prepared.element_size(), _stream(q.device)))
+    return o, lse
+
+
+def attn_split_plan(B: int, H: int, Nq: int, D: int, P: int, splits: int = 0):
+    """(split count, workspace bytes) for the split attention; splits <= 0
+    lets the library choose from the grid size."""
+    n = ctypes.c_int32(0)
+    nbytes = ctypes.c_size_t(0)
+    _check(_load().fsa_attn_split_plan(B, H, Nq, D, P, splits, ctypes.byref(n),
+                                    ctypes.byref(nbytes)))
+    return n.value, nbytes.value
+
+
+def sparse_frame_attn_split(q: torch.Tensor, k: torch.Tensor, prepared: torch.Tensor,
+                            idx: torch.Tensor, cnt: torch.Tensor, P: int, splits: int = 0,
+                            scale: float | None = None, workspace: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None):
+    """Attention with each frame list cut into `splits` parts (0: the library's
+    choice for the grid) whose partials are merged through their LSE."""
+    _need_contig(q, k, prepared, idx, cnt)
+    if idx.dtype != torch.int32 or cnt.dtype != torch.int32:
+        raise TypeError("idx and cnt must be int32")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if idx.dim() != 4 or idx.shape[:2] != (B, H) or cnt.shape != idx.shape[:3]:
+        raise ValueError("idx must be [B,H,Tq,cap] and cnt [B,H,Tq]")
+    S, nbytes = attn_split_plan(B, H, Nq, D, P, splits)
+    o = out if out is not None else torch.empty((B, H, Nq, D), dtype=torch.float32,
+                                                device=q.device)
+    lse = out_lse if out_lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
+                                                          device=q.device)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().fsa_sparse_frame_attn_prepared_split(
+        _ptr(q), _ptr(k), _ptr(prepared), _dtype_code(q), B, H, Nq, Nk, D, P, _ptr(idx),
+        _ptr(cnt), idx.shape[3], 0.0 if scale is None else float(scale), S, _ptr(o), _ptr(lse),
+        prepared.numel() * prepared.element_size(), _ptr(workspace), ws_bytes,
+        _stream(q.device)))
     return o, lse
 
 

@@ -15,8 +15,10 @@ fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *p
                                      const int32_t *idx_b, const int32_t *cnt_b, int cap_b,
                                      int B, int H, int Nq, int Nk, int D, int P, float scale,
                                      float *o_first, float *lse_first, float *o, float *lse,
-                                     hipStream_t stream);
+                                     int splits, hipStream_t stream);
 size_t attn_bf16_workspace(long long heads, int Nk, int D);
+fsa_status launch_merge_splits(const float *o_parts, const float *lse_parts, int S,
+                               long long rows, int D, float *o, float *lse, hipStream_t stream);
 }  // namespace fsa
 
 namespace {
@@ -99,7 +101,7 @@ extern "C" fsa_status fsa_sparse_frame_attn_prepared(
               "q, k, o and the prepared buffer must be 16-byte aligned");
   if (scale <= 0.f) scale = 1.f / std::sqrt((float)D);
   return fsa::launch_attn_bf16_prepared(q, k, prepared, idx, cnt, cap, nullptr, nullptr, 0, B, H,
-                                        Nq, Nk, D, P, scale, nullptr, nullptr, o, lse,
+                                        Nq, Nk, D, P, scale, nullptr, nullptr, o, lse, 1,
                                         fsa::as_stream(stream));
 }
 
@@ -126,7 +128,7 @@ extern "C" fsa_status fsa_sparse_frame_attn_dual_prepared(
               FSA_E_ARG, "q, k, the outputs and the prepared buffer must be 16-byte aligned");
   if (scale <= 0.f) scale = 1.f / std::sqrt((float)D);
   return fsa::launch_attn_bf16_prepared(q, k, prepared, idx_a, cnt_a, cap_a, idx_b, cnt_b, cap_b,
-                                        B, H, Nq, Nk, D, P, scale, o_a, lse_a, o_ab, lse_ab,
+                                        B, H, Nq, Nk, D, P, scale, o_a, lse_a, o_ab, lse_ab, 1,
                                         fsa::as_stream(stream));
 }
 
@@ -159,5 +161,76 @@ extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const 
     if (st != FSA_OK) return st;
   }
   return fsa::launch_attn_bf16_prepared(q, k, workspace, idx, cnt, cap, nullptr, nullptr, 0, B, H,
-                                        Nq, Nk, D, P, scale, nullptr, nullptr, o, lse, s);
+                                        Nq, Nk, D, P, scale, nullptr, nullptr, o, lse, 1, s);
+}
+
+namespace {
+constexpr int kMaxSplits = 16;
+constexpr long long kBlockSlots = 256 * 2;  // CUs x resident attention blocks per CU
+
+// Splits for a grid of `blocks` attention blocks.  Measured on the AR-chunk
+// shapes (468 blocks): one part is fastest for its short lists and two parts
+// gain 4 % on 49-frame lists, so parts are added only when the grid has fewer
+// blocks than compute units, enough to give every unit about two.
+int default_splits(long long blocks) {
+  if (blocks <= 0 || blocks >= 256) return 1;
+  long long s = (2 * 256 + blocks - 1) / blocks;
+  return (int)(s > 8 ? 8 : s);
+}
+}  // namespace
+
+extern "C" fsa_status fsa_attn_split_plan(int32_t B, int32_t H, int32_t Nq, int32_t D, int32_t P,
+                                          int32_t splits_req, int32_t *splits,
+                                          size_t *workspace_bytes) {
+  fsa::clear_error();
+  FSA_REQUIRE(splits && workspace_bytes, FSA_E_ARG, "null pointer argument");
+  FSA_REQUIRE(B >= 0 && H >= 0 && Nq >= 0, FSA_E_ARG, "negative size");
+  FSA_REQUIRE(D == 64 || D == 128, FSA_E_DTYPE, "head_dim D=%d is not 64 or 128", D);
+  FSA_REQUIRE(P >= 1 && Nq % P == 0, FSA_E_SHAPE, "Nq=%d is not a multiple of P=%d", Nq, P);
+  FSA_REQUIRE(splits_req <= kMaxSplits, FSA_E_ARG, "splits=%d above %d", splits_req, kMaxSplits);
+  const long long qtiles = (P + 127) / 128;
+  const int S = splits_req >= 1 ? splits_req
+                                : default_splits((long long)B * H * (Nq / P) * qtiles);
+  *splits = S;
+  *workspace_bytes = S > 1 ? (size_t)S * B * H * Nq * (size_t)(D + 1) * sizeof(float) : 0;
+  return FSA_OK;
+}
+
+extern "C" fsa_status fsa_sparse_frame_attn_prepared_split(
+    const void *q, const void *k, const void *prepared, int32_t dt, int32_t B, int32_t H,
+    int32_t Nq, int32_t Nk, int32_t D, int32_t P, const int32_t *idx, const int32_t *cnt,
+    int32_t cap, float scale, int32_t splits, float *o, float *lse, size_t prepared_bytes,
+    void *workspace, size_t workspace_bytes, void *stream) {
+  fsa::clear_error();
+  bool skip = false;
+  fsa_status st = check_attn(q, k, dt, B, H, Nq, Nk, D, P, idx, cnt, cap, scale, o, lse, &skip);
+  if (st != FSA_OK) return st;
+  FSA_REQUIRE(splits >= 1 && splits <= kMaxSplits, FSA_E_ARG, "splits=%d outside [1, %d]",
+              splits, kMaxSplits);
+  if (skip) return FSA_OK;
+  FSA_REQUIRE(dt == FSA_BF16, FSA_E_DTYPE, "prepared values exist for bf16 only");
+  const size_t need = fsa::attn_bf16_workspace((long long)B * H, Nk, D);
+  FSA_REQUIRE(need == 0 || prepared, FSA_E_ARG, "k or v is NULL");
+  FSA_REQUIRE(prepared_bytes >= need, FSA_E_CAPACITY, "prepared buffer of %zu bytes < %zu needed",
+              prepared_bytes, need);
+  const long long rows = (long long)B * H * Nq;
+  const size_t parts = splits > 1 ? (size_t)splits * rows * (size_t)(D + 1) * sizeof(float) : 0;
+  FSA_REQUIRE(parts == 0 || workspace, FSA_E_ARG, "workspace is NULL");
+  FSA_REQUIRE(workspace_bytes >= parts, FSA_E_CAPACITY, "workspace of %zu bytes < %zu needed",
+              workspace_bytes, parts);
+  FSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(prepared) && aligned16(o) &&
+                  aligned16(workspace),
+              FSA_E_ARG, "q, k, o, the workspace and the prepared buffer must be 16-byte aligned");
+  if (scale <= 0.f) scale = 1.f / std::sqrt((float)D);
+  hipStream_t s = fsa::as_stream(stream);
+  if (splits == 1)
+    return fsa::launch_attn_bf16_prepared(q, k, prepared, idx, cnt, cap, nullptr, nullptr, 0, B,
+                                          H, Nq, Nk, D, P, scale, nullptr, nullptr, o, lse, 1, s);
+  float *o_parts = static_cast<float *>(workspace);
+  float *lse_parts = o_parts + (size_t)splits * rows * D;
+  st = fsa::launch_attn_bf16_prepared(q, k, prepared, idx, cnt, cap, nullptr, nullptr, 0, B, H,
+                                      Nq, Nk, D, P, scale, nullptr, nullptr, o_parts, lse_parts,
+                                      splits, s);
+  if (st != FSA_OK) return st;
+  return fsa::launch_merge_splits(o_parts, lse_parts, splits, rows, D, o, lse, s);
 }

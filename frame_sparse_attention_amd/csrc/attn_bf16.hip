@@ -121,7 +121,8 @@ template <int D, bool DUAL>
 __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const _Float16 *__restrict__ vt, ListArg la, ListArg lb, int H, int Nq, int Nk, int NkC,
-    int P, int Tq, int qtiles, float scale_log2, OutArg first, OutArg all) {
+    int P, int Tq, int qtiles, float scale_log2, OutArg first, OutArg all, int splits,
+    long long o_split_stride, long long lse_split_stride) {
   constexpr int NCH = D / 8;                 // 16-byte chunks per K row
   constexpr int KBYTES = kTileKeys * D * 2;  // one K tile
   constexpr int VBYTES = (kTileKeys / 8) * D * 16;
@@ -140,6 +141,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
   int tile = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int qt = tile % qtiles;
   tile /= qtiles;
+  const int sp = tile % splits;  // part of the list this block attends (DUAL: always 0 of 1)
+  tile /= splits;
   const int tq = tile % Tq;
   tile /= Tq;
   const int h = tile % H;
@@ -147,9 +150,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
   const long long head = (long long)b * H + h;
   const long long list = head * Tq + tq;
   const int Tk = Nk / P;
-  // runs of list A, then (DUAL) the runs of list B after them
-  const int nruns_a =
-      build_runs(la.idx + list * la.cap, la.cnt[list], la.cap, Tk, RunList{s_lo, s_hi}, &s_nruns[0]);
+  // runs of list A (split: its entries [e0, e1)), then (DUAL) the runs of list B after them
+  int cnt_a = la.cnt[list];
+  cnt_a = cnt_a < 0 ? 0 : (cnt_a > la.cap ? la.cap : cnt_a);
+  const int e0 = (int)((long long)cnt_a * sp / splits);
+  const int e1 = (int)((long long)cnt_a * (sp + 1) / splits);
+  const int nruns_a = build_runs(la.idx + list * la.cap + e0, e1 - e0, la.cap - e0, Tk,
+                                 RunList{s_lo, s_hi}, &s_nruns[0]);
+  // a split writes its partial (O, LSE) to its own slice of the output
+  all.o += sp * o_split_stride;
+  all.lse += sp * lse_split_stride;
   int nruns = nruns_a;
   if (DUAL)
     nruns += build_runs(lb.idx + list * lb.cap, lb.cnt[list], lb.cap, Tk,
@@ -442,12 +452,13 @@ fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *p
                                      const int32_t *idx_b, const int32_t *cnt_b, int cap_b,
                                      int B, int H, int Nq, int Nk, int D, int P, float scale,
                                      float *o_first, float *lse_first, float *o, float *lse,
-                                     hipStream_t stream) {
+                                     int splits, hipStream_t stream) {
   const long long heads = (long long)B * H;
   const int NkC = (Nk + 7) / 8;
   const int Tq = Nq / P;
   const int qtiles = (P + kRows - 1) / kRows;
-  const long long blocks = heads * Tq * qtiles;
+  const long long blocks = heads * Tq * qtiles * splits;
+  const long long o_stride = heads * Nq * D, lse_stride = heads * Nq;
   FSA_REQUIRE(blocks < (1LL << 31), FSA_E_SHAPE, "too many query tiles (%lld)", blocks);
   const float scale_log2 = scale * kLog2e;
   auto qq = static_cast<const uint16_t *>(q);
@@ -460,17 +471,21 @@ fsa_status launch_attn_bf16_prepared(const void *q, const void *k, const void *p
   if (D == 64) {
     if (dual)
       hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, block, 0, stream, qq, kk, vt, la, lb,
-                         H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all);
+                         H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all, splits, o_stride,
+                         lse_stride);
     else
       hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, block, 0, stream, qq, kk, vt, la,
-                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all);
+                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all, splits, o_stride,
+                         lse_stride);
   } else {
     if (dual)
       hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, block, 0, stream, qq, kk, vt, la,
-                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all);
+                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all, splits, o_stride,
+                         lse_stride);
     else
       hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, block, 0, stream, qq, kk, vt, la,
-                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all);
+                         lb, H, Nq, Nk, NkC, P, Tq, qtiles, scale_log2, first, all, splits, o_stride,
+                         lse_stride);
   }
   return check_launch(dual ? "sparse_frame_attn_dual (bf16)" : "sparse_frame_attn (bf16)");
 }

@@ -2,7 +2,8 @@
 // (ISPA §2 item 1 and §3 item 2: decomposable attention, local and history
 // branches combined afterwards with online-softmax algebra).
 //
-// HBM-bound: reads two [rows][D] float32 partials and their LSE, writes one.
+// HBM-bound: reads two [rows][D] float32 partials and their LSE, writes one
+// (and the same for S partials of a split frame list).
 // Each group of 32 lanes owns one row; lanes stride over D so every load and
 // store of a wave covers contiguous 128-byte segments.
 #include "fsa_internal.h"
@@ -51,7 +52,60 @@ __global__ void __launch_bounds__(kThreads) merge_lse_kernel(
   }
 }
 
+// Merge of S partials of one attention (the parts of a split frame list):
+// L = M + ln sum_s exp(LSE_s - M), O = sum_s exp(LSE_s - L) O_s, in ascending
+// s; parts with LSE_s = -inf have weight 0 and are not read.  Partial s of
+// row r is o_parts[(s * rows + r) * D ...], lse_parts[s * rows + r].
+constexpr int kMaxSplits = 16;
+
+__global__ void __launch_bounds__(kThreads) merge_splits_kernel(
+    const float *__restrict__ o_parts, const float *__restrict__ lse_parts, int S, long long rows,
+    int D, float *__restrict__ o, float *__restrict__ lse) {
+  const int lane = threadIdx.x % kLanesPerRow;
+  const long long rows_per_block = kThreads / kLanesPerRow;
+  for (long long row = blockIdx.x * rows_per_block + threadIdx.x / kLanesPerRow; row < rows;
+       row += (long long)gridDim.x * rows_per_block) {
+    float ls[kMaxSplits];
+    float m = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) {
+      ls[sp] = lse_parts[sp * rows + row];
+      m = fmaxf(m, ls[sp]);
+    }
+    const long long base = row * D;
+    if (m == -INFINITY) {
+      for (int d = lane; d < D; d += kLanesPerRow) o[base + d] = 0.f;
+      if (lane == 0) lse[row] = -INFINITY;
+      continue;
+    }
+    float sum = 0.f;
+    for (int sp = 0; sp < S; ++sp) sum += ls[sp] == -INFINITY ? 0.f : expf(ls[sp] - m);
+    const float L = m + logf(sum);
+    for (int sp = 0; sp < S; ++sp) ls[sp] = ls[sp] == -INFINITY ? 0.f : expf(ls[sp] - L);
+    for (int d = lane; d < D; d += kLanesPerRow) {
+      float acc = 0.f;
+      for (int sp = 0; sp < S; ++sp)
+        if (ls[sp] != 0.f) acc += ls[sp] * o_parts[(sp * rows + row) * D + d];
+      o[base + d] = acc;
+    }
+    if (lane == 0) lse[row] = L;
+  }
+}
+
 }  // namespace
+
+namespace fsa {
+fsa_status launch_merge_splits(const float *o_parts, const float *lse_parts, int S,
+                               long long rows, int D, float *o, float *lse, hipStream_t stream) {
+  FSA_REQUIRE(S >= 1 && S <= kMaxSplits, FSA_E_ARG, "splits=%d outside [1, %d]", S, kMaxSplits);
+  if (rows == 0) return FSA_OK;
+  const long long rows_per_block = kThreads / kLanesPerRow;
+  long long blocks = (rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     o_parts, lse_parts, S, rows, D, o, lse);
+  return check_launch("merge of split partials");
+}
+}  // namespace fsa
 
 extern "C" fsa_status fsa_merge_lse(const float *o1, const float *lse1, const float *o2,
                                     const float *lse2, int64_t rows, int32_t D, float *o,

@@ -356,6 +356,33 @@ fsa_status fsa_sparse_frame_attn_prepared(const void *q, const void *k, const vo
                                           float *o, float *lse, size_t prepared_bytes,
                                           void *stream);
 
+/* device.  fsa_sparse_frame_attn_prepared with every frame list cut into
+ * `splits` parts of consecutive entries (part s holds entries
+ * [s*cnt/splits, (s+1)*cnt/splits)); each part is attended by its own blocks
+ * and the partial (O, LSE) are merged exactly through their log-sum-exp
+ * (the merge of fsa_merge_lse, over all parts in ascending order).  For grids
+ * with few query tiles (short autoregressive chunks) this spreads a long list
+ * over more compute units.  splits = 1 is fsa_sparse_frame_attn_prepared.
+ *   fsa_attn_split_plan: the split count (splits_req >= 1 is taken as given;
+ *                        <= 0 picks one from the grid size: 1 when the grid
+ *                        holds >= 256 blocks of 128 query rows, else enough
+ *                        parts for about 512 blocks, at most 8) and the
+ *                        workspace it needs, splits * B*H*Nq * (D + 1) floats
+ *                        (0 for one part)
+ *   workspace          device, >= that many bytes, 16-byte aligned (partials)
+ * Errors: as fsa_sparse_frame_attn_prepared; FSA_E_ARG (splits outside
+ * [1, 16]; workspace NULL), FSA_E_CAPACITY (workspace too small). */
+fsa_status fsa_attn_split_plan(int32_t B, int32_t H, int32_t Nq, int32_t D, int32_t P,
+                               int32_t splits_req, int32_t *splits, size_t *workspace_bytes);
+fsa_status fsa_sparse_frame_attn_prepared_split(const void *q, const void *k, const void *prepared,
+                                                int32_t dt, int32_t B, int32_t H, int32_t Nq,
+                                                int32_t Nk, int32_t D, int32_t P,
+                                                const int32_t *idx, const int32_t *cnt,
+                                                int32_t cap, float scale, int32_t splits,
+                                                float *o, float *lse, size_t prepared_bytes,
+                                                void *workspace, size_t workspace_bytes,
+                                                void *stream);
+
 /* device.  Single-pass decomposable attention [ISPA §2 item 1: the local
  * stream (current frames + sink) and the full-history stream are both
  * collected in one forward pass with negligible extra FLOPs, through the LSE

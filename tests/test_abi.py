@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(fsa.EXPORTED)
@@ -251,3 +251,39 @@ def test_rope_argument_checks(kw, status, text):
 
 def test_rope_nothing_to_do():
     assert _rope(B=0) == 0 and _rope(H=0) == 0
+
+
+def test_split_plan():
+    n = ctypes.c_int32(0)
+    nb = ctypes.c_size_t(0)
+    # 42 frames x 13 query tiles x 12 heads fill the chip: no split
+    assert lib.fsa_attn_split_plan(1, 12, 65520, 128, 1560, 0, ctypes.byref(n),
+                                   ctypes.byref(nb)) == 0
+    assert n.value == 1 and nb.value == 0
+    # a 3-frame chunk: 468 blocks fill the CUs -> one part
+    assert lib.fsa_attn_split_plan(1, 12, 4680, 128, 1560, 0, ctypes.byref(n),
+                                   ctypes.byref(nb)) == 0
+    assert n.value == 1 and nb.value == 0
+    # one 1560-token frame of 4 heads: 52 blocks -> 10 parts capped at 8
+    assert lib.fsa_attn_split_plan(1, 4, 1560, 128, 1560, 0, ctypes.byref(n),
+                                   ctypes.byref(nb)) == 0
+    assert n.value == 8 and nb.value == 8 * 4 * 1560 * 129 * 4
+    assert lib.fsa_attn_split_plan(1, 12, 4680, 128, 1560, 3, ctypes.byref(n),
+                                   ctypes.byref(nb)) == 0
+    assert n.value == 3
+    assert lib.fsa_attn_split_plan(1, 12, 4680, 128, 1560, 17, ctypes.byref(n),
+                                   ctypes.byref(nb)) == 1
+    assert lib.fsa_attn_split_plan(1, 12, 4680, 96, 1560, 2, ctypes.byref(n),
+                                   ctypes.byref(nb)) == 3
+
+
+@pytest.mark.parametrize("splits,ws_bytes,status,text", [
+    (0, 1 << 40, 1, "splits=0"),
+    (17, 1 << 40, 1, "splits=17"),
+    (4, 1000, 4, "workspace"),
+])
+def test_split_attention_argument_checks(splits, ws_bytes, status, text):
+    st = lib.fsa_sparse_frame_attn_prepared_split(BAD, BAD, BAD, 1, 1, 2, 64, 64, 128, 16, BAD,
+                                                  BAD, 4, 0.0, splits, BAD, BAD, 1 << 40, BAD,
+                                                  ws_bytes, None)
+    assert st == status and text in fsa.last_error()
