@@ -207,3 +207,23 @@ def test_dual_pass_edges(D, P):
     ru = oatt.sparse_frame_attention(qn, kn, vn, iu.numpy(), cu.numpy(), P)
     assert_close(oa.cpu().numpy(), la_.cpu().numpy(), *ra, "bf16", f"dual O_A D={D}")
     assert_close(oab.cpu().numpy(), lab.cpu().numpy(), *ru, "bf16", f"dual O_AB D={D}")
+
+
+@pytest.mark.parametrize("kind,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_maximum_list_length_and_run_count(kind, D):
+    # lists at the capacity limit (FSA_MAX_CAP = 1024 entries), a list of 512
+    # one-frame runs (every other frame), a long random list, and one frame:
+    # frames of P = 3 tokens in a 1100-frame cache, 2 query frames
+    P, Tq, Tk = 3, 4, 1100
+    rng = np.random.default_rng(12)
+    lists = [[[list(range(1024)),
+               list(range(0, 1024, 2)),
+               sorted(rng.choice(Tk, 1000, replace=False).tolist()),
+               [Tk - 1]]]]
+    idx, cnt = _lists_to_arrays(lists, 1, 1)
+    assert idx.shape[3] == 1024
+    dt = torch.bfloat16 if kind == "bf16" else torch.float32
+    q = _rand((1, 1, Tq * P, D), dt, 21)
+    k = _rand((1, 1, Tk * P, D), dt, 22)
+    v = _rand((1, 1, Tk * P, D), dt, 23)
+    _run_and_check(q, k, v, idx, cnt, P, kind, f"{kind} D={D} 1024-entry lists, 512 runs")

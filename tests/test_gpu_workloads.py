@@ -119,11 +119,23 @@ def test_decomposable_single_pass_dual_output():
                  f"{w.name} dual O_AB (all 49 frames)")
 
 
-@pytest.mark.parametrize("s", [0, 5])
+_LONG = {}
+
+
+def _long_video_inputs():
+    """The long-video tensors (the same for every step), drawn once per session."""
+    if not _LONG:
+        w = wl.long_video()
+        _say(f"{w.name}: generating inputs")
+        _LONG["qkv"] = wl.make_qkv(w)
+    return _LONG["qkv"]
+
+
+@pytest.mark.parametrize("s", range(8))
 def test_long_video_sampled_rows(s):
+    # the full denoising sweep: every step's rotated anchors
     w = wl.long_video(s)
-    _say(f"{w.name}: generating inputs")
-    q, k, v = wl.make_qkv(w)
+    q, k, v = _long_video_inputs()
     _say(f"{w.name} step {s}")
     idx, cnt, o, lse = _attn(w, q.to(DEV), k.to(DEV), v.to(DEV), w.policies)
     oidx, ocnt = ofs.build(w.policies, w.B, w.Tq, w.Tk, cap=idx.shape[3])
