@@ -16,9 +16,9 @@
 //   pool         block sums of every query block and of every key block of the
 //                candidate frames (the shared pooling kernel)
 //   frame_sums   frame sums from the block sums
-//   select       one wavefront per (b, h, query block): frame scores, kf
-//                argmax rounds, block scores over the chosen frames, kb
-//                argmax rounds, then the ascending list with the recent frames.
+//   select       one wavefront per (b, h, query block): frame scores, the kf
+//                best by rank, block scores over the chosen frames, the kb best
+//                by rank, then the ascending list with the recent frames.
 #pragma clang fp contract(off)
 
 #include "pooling.h"
@@ -47,10 +47,24 @@ __device__ inline bool hsa_better(double s1, int i1, double s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
-// k rounds of a wavefront argmax over s_score[0..n) not yet taken; marks the
-// winners in s_taken.  Needs k <= n.
+// Marks in s_taken the k best of s_score[0..n) in the (score descending,
+// index ascending) order, a strict total order: up to 1024 candidates, each
+// lane counts for its candidates how many others come first and keeps those
+// with fewer than k (one pass of n comparisons per candidate); beyond that, k
+// rounds of a wavefront argmax.  Both give the same set.  Needs k <= n and
+// s_taken[0..n) cleared.
 __device__ void take_best(const double *s_score, unsigned char *s_taken, int n, int k) {
   const int lane = threadIdx.x;
+  if (n <= 1024) {
+    for (int i = lane; i < n; i += 64) {
+      const double si = s_score[i];
+      int ahead = 0;
+      for (int j = 0; j < n; ++j) ahead += hsa_better(s_score[j], j, si, i) ? 1 : 0;
+      s_taken[i] = ahead < k ? 1 : 0;
+    }
+    __syncthreads();
+    return;
+  }
   for (int round = 0; round < k; ++round) {
     double bs = 0.0;
     int bi = -1;
@@ -116,12 +130,7 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   // level 1: frames
   const double *kf_base = kframe + bh * Fc * D;
   for (int f = lane; f < first_recent; f += 64) {
-    double acc = 0.0;
-    for (int d = 0; d < D; ++d) {
-      const double prod = qs[d] * kf_base[(long long)f * D + d];
-      acc = acc + prod;
-    }
-    s_score[f] = acc;
+    s_score[f] = ordered_dot(qs, kf_base + (long long)f * D, D);
     s_taken[f] = 0;
   }
   __syncthreads();
@@ -135,12 +144,7 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   const double *kb_base = kblk + bh * (long long)Fc * nb * D;
   for (int c = lane; c < nbc; c += 64) {
     const long long blk = (long long)s_frames[c / nb] * nb + c % nb;
-    double acc = 0.0;
-    for (int d = 0; d < D; ++d) {
-      const double prod = qs[d] * kb_base[blk * D + d];
-      acc = acc + prod;
-    }
-    s_score[c] = acc;
+    s_score[c] = ordered_dot(qs, kb_base + blk * D, D);
     s_taken[c] = 0;
   }
   __syncthreads();

@@ -171,13 +171,153 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(
   }
 }
 
-// Launches pool_kernel for every query segment [t*P, (t+1)*P) of Nq and every
-// key segment cand_begin + fi, fi < F, of the heads [h_begin, h_begin + Hs).
+// One wavefront per segment, for rows of a power-of-two size between 16 and
+// 1024 bytes and D <= 128 even: lane t adds channels 2t and 2t+1 (two
+// independent float64 chains, each in ascending row order).  Rows stream
+// through an LDS ring of kWaveRing chunks of 16 KB with global_load_lds,
+// kWaveRing - 1 chunks ahead; a single wavefront needs no barrier, since its
+// own vmcnt wait makes a chunk visible and the reads of a slot finish before
+// the adds that use them, i.e. before the slot is refilled.
+constexpr int kWaveRing = 4;
+constexpr int kWaveChunk = 16384;  // bytes per ring slot: 16 DMA instructions of 1 KB
+
+template <typename T>
+__device__ inline void pair_as_double(const unsigned char *p, double &x0, double &x1);
+template <>
+__device__ inline void pair_as_double<float>(const unsigned char *p, double &x0, double &x1) {
+  const float2 v = *reinterpret_cast<const float2 *>(p);
+  x0 = (double)v.x;
+  x1 = (double)v.y;
+}
+template <>
+__device__ inline void pair_as_double<Bf16>(const unsigned char *p, double &x0, double &x1) {
+  const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+  x0 = (double)__uint_as_float(w << 16);
+  x1 = (double)__uint_as_float(w & 0xFFFF0000u);
+}
+
+template <typename T>
+__device__ void pool_segment_wave(const T *__restrict__ src, long long row0, int nrows, int D,
+                                  double *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kWaveRing][kWaveChunk];
+  const int lane = threadIdx.x;
+  const int row_bytes = D * (int)sizeof(T);
+  const int rows_per_chunk = kWaveChunk / row_bytes;
+  const int nchunks = (nrows + rows_per_chunk - 1) / rows_per_chunk;
+  const char *base = reinterpret_cast<const char *>(src) + row0 * row_bytes;
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kWaveChunk / 1024; ++i) {
+      const int unit = i * 64 + lane;  // 16-byte unit of the chunk
+      int r = c * rows_per_chunk + unit * 16 / row_bytes;
+      r = r < nrows ? r : nrows - 1;  // past the segment: repeat its last row (never added)
+      const char *g = base + (long long)r * row_bytes + (unit * 16) % row_bytes;
+      __builtin_amdgcn_global_load_lds(
+          (const void *)g, (__attribute__((address_space(3))) void *)&ring[c % kWaveRing][i * 1024],
+          16, 0, 0);
+    }
+  };
+  const int ch = 2 * lane;
+  const bool active = ch < D;
+  double a0 = 0.0, a1 = 0.0;
+  for (int c = 0; c < kWaveRing - 1 && c < nchunks; ++c) issue(c);
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + kWaveRing - 1 < nchunks) {
+      issue(c + kWaveRing - 1);
+      wait_vmcnt<(kWaveChunk / 1024) * (kWaveRing - 1)>();  // chunk c has landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    const int rows = min(rows_per_chunk, nrows - c * rows_per_chunk);
+    const unsigned char *t = ring[c % kWaveRing];
+    if (active) {
+      for (int r = 0; r < rows; ++r) {
+        double x0, x1;
+        pair_as_double<T>(t + r * row_bytes + ch * (int)sizeof(T), x0, x1);
+        a0 = a0 + x0;
+        a1 = a1 + x1;
+      }
+    }
+  }
+  if (active) {
+    out[ch] = a0;
+    out[ch + 1] = a1;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(64) pool_wave_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, int H, int Nq, int Nk, int D, int P,
+    int h_begin, int Hs, int Tq, int cand_begin, int F, double *__restrict__ qframe,
+    double *__restrict__ ksum) {
+  const long long bid = blockIdx.x;
+  // layout: b-major, then [Tq query segments | F key segments] per selected head
+  const int per_b = Hs * (Tq + F);
+  const int b = (int)(bid / per_b);
+  const int rem = (int)(bid % per_b);
+  if (rem < Hs * Tq) {
+    const int hs = rem / Tq, t = rem % Tq;
+    const long long head = (long long)b * H + h_begin + hs;
+    pool_segment_wave<T>(q, head * Nq + (long long)t * P, P, D,
+                         qframe + ((long long)(b * Hs + hs) * Tq + t) * D);
+  } else {
+    const int r2 = rem - Hs * Tq;
+    const int hs = r2 / F, fi = r2 % F;
+    const long long head = (long long)b * H + h_begin + hs;
+    pool_segment_wave<T>(k, head * Nk + (long long)(cand_begin + fi) * P, P, D,
+                         ksum + ((long long)(b * Hs + hs) * F + fi) * D);
+  }
+}
+
+// sum_d qs[d] * row[d] in ascending d, each product rounded before it is
+// added.  The row (global memory) is read 16 values at a time into registers
+// ahead of the ordered adds, so the loads overlap instead of each add waiting
+// for its own load.
+__device__ inline double ordered_dot(const double *qs, const double *__restrict__ row, int D) {
+  double acc = 0.0;
+  int d0 = 0;
+  if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) {
+    for (; d0 + 16 <= D; d0 += 16) {
+      double2 x[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) x[t] = reinterpret_cast<const double2 *>(row + d0)[t];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const double p0 = qs[d0 + 2 * t] * x[t].x;
+        acc = acc + p0;
+        const double p1 = qs[d0 + 2 * t + 1] * x[t].y;
+        acc = acc + p1;
+      }
+    }
+  }
+  for (; d0 < D; ++d0) {
+    const double p = qs[d0] * row[d0];
+    acc = acc + p;
+  }
+  return acc;
+}
+
+// Pools every query segment [t*P, (t+1)*P) of Nq and every key segment
+// cand_begin + fi, fi < F, of the heads [h_begin, h_begin + Hs): one wavefront
+// per segment where the rows allow it, else pool_kernel.
 inline void launch_pool(int32_t dt, const void *q, const void *k, int H, int Nq, int Nk, int D,
                         int P, int h_begin, int Hs, int Tq, int cand_begin, int F, long long blocks,
                         double *qframe, double *ksum, hipStream_t s) {
   const bool aligned =
       ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15u) == 0;
+  const int row_bytes = D * (dt == FSA_BF16 ? 2 : 4);
+  const bool pow2_row = row_bytes >= 16 && row_bytes <= 1024 && (row_bytes & (row_bytes - 1)) == 0;
+  if (aligned && pow2_row && D % 2 == 0 && D <= 128) {
+    if (dt == FSA_BF16)
+      hipLaunchKernelGGL(pool_wave_kernel<Bf16>, dim3((unsigned)blocks), dim3(64), 0, s,
+                         static_cast<const Bf16 *>(q), static_cast<const Bf16 *>(k), H, Nq, Nk,
+                         D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+    else
+      hipLaunchKernelGGL(pool_wave_kernel<float>, dim3((unsigned)blocks), dim3(64), 0, s,
+                         static_cast<const float *>(q), static_cast<const float *>(k), H, Nq, Nk,
+                         D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+    return;
+  }
   if (dt == FSA_BF16) {
     const size_t chunk = (size_t)kRowsPerChunk * D * sizeof(Bf16);
     const size_t lds = aligned && chunk * kRing <= 65536 ? chunk * kRing : chunk;

@@ -12,8 +12,9 @@
 //   pool          one block per (b, h, query frame) and per (b, h, key frame):
 //                 rows staged through LDS, one sequential float64 chain per
 //                 channel; every token is read once
-//   score_select  one wavefront per (b, h, group): scores, then k rounds of a
-//                 wavefront argmax on (score desc, frame asc), then sorting.
+//   score_select  one wavefront per (b, h, group): scores, then the k best on
+//                 (score desc, frame asc) by rank (k rounds of a wavefront
+//                 argmax beyond 1024 candidates), written in ascending order.
 #pragma clang fp contract(off)
 
 #include "pooling.h"
@@ -50,16 +51,34 @@ __global__ void __launch_bounds__(64) score_select_kernel(
   const double *ks = ksum + (long long)(b * Hs + hs) * F * D;
   const long long out_head = (long long)b * H + h_begin + hs;
   for (int fi = lane; fi < F; fi += 64) {
-    double acc = 0.0;
-    for (int d = 0; d < D; ++d) {
-      const double prod = qs[d] * ks[(long long)fi * D + d];
-      acc = acc + prod;
-    }
+    const double acc = ordered_dot(qs, ks + (long long)fi * D, D);
     s_score[fi] = acc;
     s_taken[fi] = 0;
     if (out_scores) out_scores[(out_head * G + g) * F + fi] = acc;
   }
   __syncthreads();
+  int32_t *out = out_frames + (out_head * G + g) * topk;
+  if (F <= 1024) {
+    // the topk best by rank: a candidate is kept when fewer than topk others
+    // come first in the strict (score desc, frame asc) order
+    for (int fi = lane; fi < F; fi += 64) {
+      const double si = s_score[fi];
+      int ahead = 0;
+      for (int j = 0; j < F; ++j) ahead += better(s_score[j], j, si, fi) ? 1 : 0;
+      s_taken[fi] = ahead < topk ? 1 : 0;
+    }
+    __syncthreads();
+    // ascending frames: position = kept candidates before this one
+    int count = 0;
+    for (int base = 0; base < F; base += 64) {
+      const int fi = base + lane;
+      const bool keep = fi < F && s_taken[fi];
+      const unsigned long long mask = __ballot(keep);
+      if (keep) out[count + __popcll(mask & ((1ull << lane) - 1ull))] = cand_begin + fi;
+      count += __popcll(mask);
+    }
+    return;
+  }
   int mine = -1;  // frame selected in round == lane
   for (int round = 0; round < topk; ++round) {
     double bs = 0.0;
@@ -90,7 +109,7 @@ __global__ void __launch_bounds__(64) score_select_kernel(
     const int other = __shfl(mine, j);
     if (other < mine) ++rank;
   }
-  if (lane < topk) out_frames[(out_head * G + g) * topk + rank] = cand_begin + mine;
+  if (lane < topk) out[rank] = cand_begin + mine;
 }
 
 fsa_status check_args(int32_t B, int32_t H, int32_t Nq, int32_t D, int32_t P, int32_t q_group,

@@ -183,3 +183,18 @@ def test_merge_in_place():
     fsa.merge_lse(a, la, o2.to(DEV), l2.to(DEV), out=a, out_lse=la)
     torch.cuda.synchronize()
     assert torch.equal(a, ref_o) and torch.equal(la, ref_l)
+
+
+@pytest.mark.parametrize("n_cand,kk", [(1024, 64), (1025, 7), (3000, 40)])
+def test_topk_many_candidates(n_cand, kk):
+    # at most 1024 candidates the k best are taken by rank, beyond that by
+    # rounds of a wavefront argmax: both must give the oracle's frames
+    g = torch.Generator().manual_seed(n_cand)
+    B, H, P, D = 1, 2, 2, 64
+    q = torch.randn(B, H, 2 * P, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, H, n_cand * P, D, generator=g).to(torch.bfloat16)
+    _say(f"top-k over {n_cand} candidates, k={kk}")
+    frames = fsa.select_topk_frames(q.to(DEV), k.to(DEV), P, 0, H, 2, 0, n_cand, kk)
+    torch.cuda.synchronize()
+    of, _ = _oracle_topk(q, k, P, 0, H, 2, 0, n_cand, kk)
+    np.testing.assert_array_equal(frames.cpu().numpy(), of)

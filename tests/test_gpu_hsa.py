@@ -51,6 +51,8 @@ CASES = [
     ("bf16", 1, 2, 128, 2, 8, 16, 8, 6, 2, 0, 2, 0, 6, 1),      # no recent frames, kb = 1
     ("bf16", 1, 1, 128, 1, 6, 24, 24, 5, 1, 0, 1, 2, 4, 4),     # blocks as large as frames
     ("bf16", 1, 2, 128, 2, 7, 16, 4, 5, 2, 0, 2, 2, 2, 0),      # kb = 0: recent frames only
+    ("bf16", 1, 1, 64, 1, 40, 128, 2, 39, 1, 0, 1, 1, 20, 300),  # 1280 candidate blocks
+    ("bf16", 1, 1, 64, 1, 1100, 2, 2, 1099, 1, 0, 1, 1, 1030, 9),  # 1098 candidate frames
 ]
 
 
