@@ -15,7 +15,7 @@ constexpr int kThreads = 256;
 
 __global__ void __launch_bounds__(kThreads) merge_lse_kernel(
     const float *o1, const float *lse1, const float *o2, const float *lse2, long long rows,
-    int D, float *o, float *lse) {
+    int D, bool vec4, float *o, float *lse) {
   const int lane = threadIdx.x % kLanesPerRow;
   const long long rows_per_block = kThreads / kLanesPerRow;
   for (long long row = blockIdx.x * rows_per_block + threadIdx.x / kLanesPerRow; row < rows;
@@ -40,11 +40,27 @@ __global__ void __launch_bounds__(kThreads) merge_lse_kernel(
       wb = expf(b - L);
     }
     const long long base = row * D;
-    for (int d = lane; d < D; d += kLanesPerRow) {
-      // a zero weight must not touch the other operand (it may hold anything)
-      float x = wa != 0.f ? wa * o1[base + d] : 0.f;
-      float y = wb != 0.f ? wb * o2[base + d] : 0.f;
-      o[base + d] = x + y;
+    if (vec4) {
+      // 16-byte accesses: lane t covers channels 4t .. 4t+3 of each 128-channel span
+      for (int d = 4 * lane; d < D; d += 4 * kLanesPerRow) {
+        const float4 a = wa != 0.f ? *reinterpret_cast<const float4 *>(o1 + base + d)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 c = wb != 0.f ? *reinterpret_cast<const float4 *>(o2 + base + d)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 r;
+        r.x = (wa != 0.f ? wa * a.x : 0.f) + (wb != 0.f ? wb * c.x : 0.f);
+        r.y = (wa != 0.f ? wa * a.y : 0.f) + (wb != 0.f ? wb * c.y : 0.f);
+        r.z = (wa != 0.f ? wa * a.z : 0.f) + (wb != 0.f ? wb * c.z : 0.f);
+        r.w = (wa != 0.f ? wa * a.w : 0.f) + (wb != 0.f ? wb * c.w : 0.f);
+        *reinterpret_cast<float4 *>(o + base + d) = r;
+      }
+    } else {
+      for (int d = lane; d < D; d += kLanesPerRow) {
+        // a zero weight must not touch the other operand (it may hold anything)
+        float x = wa != 0.f ? wa * o1[base + d] : 0.f;
+        float y = wb != 0.f ? wb * o2[base + d] : 0.f;
+        o[base + d] = x + y;
+      }
     }
     // Every lane of this row has read lse1/lse2 above (the 32 lanes of a row
     // sit in one wavefront and execute in lockstep), so an aliased write is safe.
@@ -118,7 +134,9 @@ extern "C" fsa_status fsa_merge_lse(const float *o1, const float *lse1, const fl
   const long long rows_per_block = kThreads / kLanesPerRow;
   long long blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (blocks > 65536) blocks = 65536;
+  const bool vec4 = D % 4 == 0 && ((reinterpret_cast<uintptr_t>(o1) | reinterpret_cast<uintptr_t>(o2) |
+                                    reinterpret_cast<uintptr_t>(o)) & 15u) == 0;
   hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                     fsa::as_stream(stream), o1, lse1, o2, lse2, (long long)rows, D, o, lse);
+                     fsa::as_stream(stream), o1, lse1, o2, lse2, (long long)rows, D, vec4, o, lse);
   return fsa::check_launch("merge_lse");
 }
