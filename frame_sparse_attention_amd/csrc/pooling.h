@@ -174,11 +174,10 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(
 // One wavefront per segment, for rows of a power-of-two size between 16 and
 // 1024 bytes and D <= 128 even: lane t adds channels 2t and 2t+1 (two
 // independent float64 chains, each in ascending row order).  Rows stream
-// through an LDS ring of kWaveRing chunks of 16 KB with global_load_lds,
+// through an LDS ring of kWaveRing (2 or 4) chunks of 16 KB with global_load_lds,
 // kWaveRing - 1 chunks ahead; a single wavefront needs no barrier, since its
 // own vmcnt wait makes a chunk visible and the reads of a slot finish before
 // the adds that use them, i.e. before the slot is refilled.
-constexpr int kWaveRing = 4;
 constexpr int kWaveChunk = 16384;  // bytes per ring slot: 16 DMA instructions of 1 KB
 
 template <typename T>
@@ -196,29 +195,35 @@ __device__ inline void pair_as_double<Bf16>(const unsigned char *p, double &x0, 
   x1 = (double)__uint_as_float(w & 0xFFFF0000u);
 }
 
-template <typename T>
+template <typename T, int kWaveRing, int CSPLIT>
 __device__ void pool_segment_wave(const T *__restrict__ src, long long row0, int nrows, int D,
-                                  double *__restrict__ out) {
+                                  int cgroup, double *__restrict__ out) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[kWaveRing][kWaveChunk];
   const int lane = threadIdx.x;
-  const int row_bytes = D * (int)sizeof(T);
+  // this wavefront's channels: [cgroup * D / CSPLIT, (cgroup + 1) * D / CSPLIT)
+  const int Dw = D / CSPLIT;
+  const int row_stride = D * (int)sizeof(T);       // bytes between rows in memory
+  const int row_bytes = Dw * (int)sizeof(T);       // bytes of a row this wavefront stages
+  const int col0 = cgroup * row_bytes;
   const int rows_per_chunk = kWaveChunk / row_bytes;
   const int nchunks = (nrows + rows_per_chunk - 1) / rows_per_chunk;
-  const char *base = reinterpret_cast<const char *>(src) + row0 * row_bytes;
+  const char *base = reinterpret_cast<const char *>(src) + row0 * row_stride;
   auto issue = [&](int c) {
 #pragma unroll
     for (int i = 0; i < kWaveChunk / 1024; ++i) {
       const int unit = i * 64 + lane;  // 16-byte unit of the chunk
       int r = c * rows_per_chunk + unit * 16 / row_bytes;
       r = r < nrows ? r : nrows - 1;  // past the segment: repeat its last row (never added)
-      const char *g = base + (long long)r * row_bytes + (unit * 16) % row_bytes;
+      const char *g = base + (long long)r * row_stride + col0 + (unit * 16) % row_bytes;
       __builtin_amdgcn_global_load_lds(
           (const void *)g, (__attribute__((address_space(3))) void *)&ring[c % kWaveRing][i * 1024],
           16, 0, 0);
     }
   };
-  const int ch = 2 * lane;
-  const bool active = ch < D;
+  // CSPLIT == 1: lane t adds channels 2t, 2t+1; CSPLIT == 2: lane t adds channel t
+  constexpr int kCh = CSPLIT == 1 ? 2 : 1;
+  const int ch = kCh * lane;
+  const bool active = ch < Dw;
   double a0 = 0.0, a1 = 0.0;
   for (int c = 0; c < kWaveRing - 1 && c < nchunks; ++c) issue(c);
   for (int c = 0; c < nchunks; ++c) {
@@ -231,26 +236,32 @@ __device__ void pool_segment_wave(const T *__restrict__ src, long long row0, int
     const int rows = min(rows_per_chunk, nrows - c * rows_per_chunk);
     const unsigned char *t = ring[c % kWaveRing];
     if (active) {
-      for (int r = 0; r < rows; ++r) {
-        double x0, x1;
-        pair_as_double<T>(t + r * row_bytes + ch * (int)sizeof(T), x0, x1);
-        a0 = a0 + x0;
-        a1 = a1 + x1;
+      if (kCh == 2) {
+        for (int r = 0; r < rows; ++r) {
+          double x0, x1;
+          pair_as_double<T>(t + r * row_bytes + ch * (int)sizeof(T), x0, x1);
+          a0 = a0 + x0;
+          a1 = a1 + x1;
+        }
+      } else {
+        for (int r = 0; r < rows; ++r)
+          a0 = a0 + elem_as_double<T>(reinterpret_cast<const T *>(t + r * row_bytes), 0, ch, 0);
       }
     }
   }
   if (active) {
-    out[ch] = a0;
-    out[ch + 1] = a1;
+    out[cgroup * Dw + ch] = a0;
+    if (kCh == 2) out[cgroup * Dw + ch + 1] = a1;
   }
 }
 
-template <typename T>
+template <typename T, int kWaveRing, int CSPLIT>
 __global__ void __launch_bounds__(64) pool_wave_kernel(
     const T *__restrict__ q, const T *__restrict__ k, int H, int Nq, int Nk, int D, int P,
     int h_begin, int Hs, int Tq, int cand_begin, int F, double *__restrict__ qframe,
     double *__restrict__ ksum) {
-  const long long bid = blockIdx.x;
+  const long long bid = blockIdx.x / CSPLIT;
+  const int cgroup = (int)(blockIdx.x % CSPLIT);
   // layout: b-major, then [Tq query segments | F key segments] per selected head
   const int per_b = Hs * (Tq + F);
   const int b = (int)(bid / per_b);
@@ -258,13 +269,14 @@ __global__ void __launch_bounds__(64) pool_wave_kernel(
   if (rem < Hs * Tq) {
     const int hs = rem / Tq, t = rem % Tq;
     const long long head = (long long)b * H + h_begin + hs;
-    pool_segment_wave<T>(q, head * Nq + (long long)t * P, P, D,
+    pool_segment_wave<T, kWaveRing, CSPLIT>(q, head * Nq + (long long)t * P, P, D, cgroup,
                          qframe + ((long long)(b * Hs + hs) * Tq + t) * D);
   } else {
     const int r2 = rem - Hs * Tq;
     const int hs = r2 / F, fi = r2 % F;
     const long long head = (long long)b * H + h_begin + hs;
-    pool_segment_wave<T>(k, head * Nk + (long long)(cand_begin + fi) * P, P, D,
+    pool_segment_wave<T, kWaveRing, CSPLIT>(k, head * Nk + (long long)(cand_begin + fi) * P, P, D,
+                                            cgroup,
                          ksum + ((long long)(b * Hs + hs) * F + fi) * D);
   }
 }
@@ -308,14 +320,38 @@ inline void launch_pool(int32_t dt, const void *q, const void *k, int H, int Nq,
   const int row_bytes = D * (dt == FSA_BF16 ? 2 : 4);
   const bool pow2_row = row_bytes >= 16 && row_bytes <= 1024 && (row_bytes & (row_bytes - 1)) == 0;
   if (aligned && pow2_row && D % 2 == 0 && D <= 128) {
-    if (dt == FSA_BF16)
-      hipLaunchKernelGGL(pool_wave_kernel<Bf16>, dim3((unsigned)blocks), dim3(64), 0, s,
-                         static_cast<const Bf16 *>(q), static_cast<const Bf16 *>(k), H, Nq, Nk,
-                         D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
-    else
-      hipLaunchKernelGGL(pool_wave_kernel<float>, dim3((unsigned)blocks), dim3(64), 0, s,
-                         static_cast<const float *>(q), static_cast<const float *>(k), H, Nq, Nk,
-                         D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+    // segments of at most two chunks fit a two-slot ring: smaller LDS, more
+    // wavefronts per CU; longer segments stream through four slots, and when
+    // a half row is still 128 bytes or more their channels are split over two
+    // wavefronts (one ordered chain per lane, half the instructions each)
+    const bool short_seg = P <= 2 * (kWaveChunk / row_bytes);
+    const bool split = !short_seg && row_bytes >= 256;
+    const dim3 grid((unsigned)(blocks * (split ? 2 : 1))), block(64);
+    if (dt == FSA_BF16) {
+      auto qq = static_cast<const Bf16 *>(q);
+      auto kk = static_cast<const Bf16 *>(k);
+      if (short_seg)
+        hipLaunchKernelGGL((pool_wave_kernel<Bf16, 2, 1>), grid, block, 0, s, qq, kk, H, Nq, Nk,
+                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+      else if (split)
+        hipLaunchKernelGGL((pool_wave_kernel<Bf16, 4, 2>), grid, block, 0, s, qq, kk, H, Nq, Nk,
+                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+      else
+        hipLaunchKernelGGL((pool_wave_kernel<Bf16, 4, 1>), grid, block, 0, s, qq, kk, H, Nq, Nk,
+                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+    } else {
+      auto qq = static_cast<const float *>(q);
+      auto kk = static_cast<const float *>(k);
+      if (short_seg)
+        hipLaunchKernelGGL((pool_wave_kernel<float, 2, 1>), grid, block, 0, s, qq, kk, H, Nq, Nk,
+                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+      else if (split)
+        hipLaunchKernelGGL((pool_wave_kernel<float, 4, 2>), grid, block, 0, s, qq, kk, H, Nq, Nk,
+                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+      else
+        hipLaunchKernelGGL((pool_wave_kernel<float, 4, 1>), grid, block, 0, s, qq, kk, H, Nq, Nk,
+                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+    }
     return;
   }
   if (dt == FSA_BF16) {
