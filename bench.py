@@ -309,6 +309,9 @@ def main() -> int:
     w = wl.lvsa_shaped()
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = wl.make_qkv(w)
+    # identity of the timed inputs: sha256 of the raw bf16 bytes of q, k and v
+    inputs_sha256 = {n: hashlib.sha256(t.view(torch.int16).numpy().tobytes()).hexdigest()
+                     for n, t in zip("qkv", (q, k, v))}
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     cap = fsa.frame_set_capacity(w.policies, w.Tq, w.Tk)
     idx = torch.empty((w.B, w.H, w.Tq, cap), dtype=torch.int32, device=dev)
@@ -387,6 +390,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), 4 outlier channels x8, bf16)",
+        "inputs_sha256": inputs_sha256,
         "config": {"workload": w.name, "B": w.B, "heads": w.H, "head_dim": w.D,
                    "frames": w.Tq, "tokens_per_frame": w.P, "budget_C": 21, "window_W": 7,
                    "T_per": 6, "denoise_steps_rotated": w.steps,
