@@ -198,3 +198,25 @@ def test_topk_many_candidates(n_cand, kk):
     torch.cuda.synchronize()
     of, _ = _oracle_topk(q, k, P, 0, H, 2, 0, n_cand, kk)
     np.testing.assert_array_equal(frames.cpu().numpy(), of)
+
+
+@pytest.mark.parametrize("dtype,D,P", [
+    (torch.float32, 128, 300),   # long segments, channels split over two wavefronts
+    (torch.float32, 64, 500),    # float32 half rows of 128 bytes: split as well
+    (torch.bfloat16, 64, 700),   # 128-byte rows: one wavefront, four-slot ring
+    (torch.bfloat16, 128, 100),  # short segments: two-slot ring
+    (torch.bfloat16, 96, 90),    # 192-byte rows: the block-per-segment kernel
+    (torch.float32, 200, 40),    # 800-byte rows: the block-per-segment kernel
+])
+def test_topk_pooling_paths(dtype, D, P):
+    g = torch.Generator().manual_seed(D * 1000 + P)
+    B, H = 1, 2
+    q = (torch.randn(B, H, 2 * P, D, generator=g) * 3).to(dtype)
+    k = (torch.randn(B, H, 12 * P, D, generator=g) * 3).to(dtype)
+    _say(f"top-k pooling path {dtype} D={D} P={P}")
+    frames, scores = fsa.select_topk_frames(q.to(DEV), k.to(DEV), P, 0, H, 2, 0, 12, 4,
+                                            return_scores=True)
+    torch.cuda.synchronize()
+    of, os_ = _oracle_topk(q, k, P, 0, H, 2, 0, 12, 4)
+    np.testing.assert_array_equal(frames.cpu().numpy(), of)
+    assert np.array_equal(scores.cpu().numpy(), os_)
