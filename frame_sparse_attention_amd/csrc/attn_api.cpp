@@ -166,15 +166,16 @@ extern "C" fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const 
 
 namespace {
 constexpr int kMaxSplits = 16;
-constexpr long long kBlockSlots = 256 * 2;  // CUs x resident attention blocks per CU
+constexpr long long kCUs = 256;                // compute units of an MI355X
+constexpr long long kBlockSlots = kCUs * 2;     // resident attention blocks: two per CU
 
 // Splits for a grid of `blocks` attention blocks.  Measured on the AR-chunk
 // shapes (468 blocks): one part is fastest for its short lists and two parts
 // gain 4 % on 49-frame lists, so parts are added only when the grid has fewer
 // blocks than compute units, enough to give every unit about two.
 int default_splits(long long blocks) {
-  if (blocks <= 0 || blocks >= 256) return 1;
-  long long s = (2 * 256 + blocks - 1) / blocks;
+  if (blocks <= 0 || blocks >= kCUs) return 1;
+  long long s = (kBlockSlots + blocks - 1) / blocks;
   return (int)(s > 8 ? 8 : s);
 }
 }  // namespace
