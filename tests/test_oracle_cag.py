@@ -62,3 +62,40 @@ def test_zero_target_is_dense_and_limits_raise():
 
 def test_frame_budgets():
     assert cag.frame_budgets([0.5, 0.75, 0.99, 0.0, 0.3], [7, 2, 3, 9, 10]) == [4, 1, 1, 9, 7]
+
+
+@pytest.mark.parametrize("n,sb,smax", [(2, 0.5, 0.9), (7, 0.8, 0.6), (60, 0.6, 0.95), (3, 0.0, 0.5)])
+def test_bracket_clips_every_chunk_at_each_end(n, sb, smax):
+    # The bisection's bracket: at its low end every later chunk sits at s_max,
+    # at its high end every one at 0; chunk 0 is dense at both.
+    lo, hi = cag.bracket(n, sb, smax)
+    s_lo, s_hi = cag.sparsity_at(lo, n, sb, smax), cag.sparsity_at(hi, n, sb, smax)
+    assert s_lo[0] == 0.0 and s_hi[0] == 0.0
+    assert all(v == smax for v in s_lo[1:])
+    assert all(v == 0.0 for v in s_hi[1:])
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.05, 0.3, 1.0, -0.2])
+def test_sparsity_profile_is_monotone_and_bounded(beta):
+    n, sb, smax = 40, 0.7, 0.85
+    s = cag.sparsity_at(beta, n, sb, smax)
+    assert s[0] == 0.0 and all(0.0 <= v <= smax for v in s)
+    later = s[1:]
+    if beta >= 0:   # the weight of beta falls with i, so later chunks are sparser, up to s_base
+        assert all(a <= b for a, b in zip(later, later[1:]))
+        assert all(v <= sb for v in later)
+    else:           # a negative beta pushes early chunks above s_base instead
+        assert all(a >= b for a, b in zip(later, later[1:]))
+        assert all(v >= min(sb, smax) for v in later)
+    if beta == 0.0:
+        assert later == [min(sb, smax)] * (n - 1)
+
+
+def test_kept_cost_endpoints_and_monotone_in_beta():
+    cost = [4.0, 1.0, 2.0, 8.0, 16.0]
+    assert cag.kept_cost([0.0] * 5, cost) == 31.0                       # dense: every cost kept
+    assert cag.kept_cost([0.0, 0.5, 0.5, 0.5, 0.5], cost) == 4.0 + 13.5  # exact halves
+    n, sb, smax = len(cost), 0.6, 0.9
+    betas = [-1.0 + 0.05 * i for i in range(60)]
+    kept = [cag.kept_cost(cag.sparsity_at(b, n, sb, smax), cost) for b in betas]
+    assert all(a <= b for a, b in zip(kept, kept[1:]))

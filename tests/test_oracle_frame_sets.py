@@ -145,3 +145,18 @@ def test_range_and_full():
     assert fs.frame_range(1, 45, 49) == list(range(1, 46))
     assert fs.frame_range(-3, 100, 5) == [0, 1, 2, 3, 4]
     assert fs.full(4) == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("offset,chunk", [(0, 1), (57, 3), (5, 4), (0, 7)])
+def test_chunk_last_frame_is_the_chunks_last_kv_frame(offset, chunk):
+    # A chunk covers query frames [c*chunk, (c+1)*chunk), i.e. KV frames
+    # offset + c*chunk .. offset + (c+1)*chunk - 1; every member maps to the last.
+    for tq in range(4 * chunk):
+        e = fs.chunk_last_frame(tq, chunk, offset)
+        assert 0 <= e - (offset + tq) < chunk
+        assert (e - offset + 1) % chunk == 0
+        first = tq - tq % chunk
+        assert all(fs.chunk_last_frame(u, chunk, offset) == e for u in range(first, first + chunk))
+    # the AR workload: query frames 0..2 at KV frames 57..59 form one chunk ending at 59
+    if (offset, chunk) == (57, 3):
+        assert [fs.chunk_last_frame(t, 3, 57) for t in range(3)] == [59, 59, 59]
