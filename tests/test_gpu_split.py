@@ -21,14 +21,16 @@ def _say(msg):
     print(f"[gpu] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
-def test_split_counts_small(splits):
-    # 3 heads: a 1-frame list (most parts empty), a 4-frame window, all 9 frames
-    w = wl.Workload("split_small", 70, 1, 3, 128, 3, 9, 40, "bf16",
+@pytest.mark.parametrize("splits,D", [(1, 128), (2, 128), (3, 128), (7, 128), (16, 128),
+                                      (0, 128), (3, 64), (16, 64)])
+def test_split_counts_small(splits, D):
+    # 3 heads: a 1-frame list (most parts empty), a 4-frame window, all 9 frames;
+    # splits = 0 takes the library's default plan
+    w = wl.Workload("split_small", 70, 1, 3, D, 3, 9, 40, "bf16",
                     [wl.policy(wl.SINK_WINDOW, n_sink=0, window=1),
                      wl.policy(wl.SINK_WINDOW, n_sink=1, window=3),
                      wl.policy(wl.FULL)], offset=6, chunk=1)
-    _say(f"split attention, {splits} parts")
+    _say(f"split attention, {splits} parts, D={D}")
     q, k, v = wl.make_qkv(w)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     idx, cnt = fsa.build_frame_sets(w.policies, w.B, w.Tq, w.Tk, w.offset, w.chunk, device=DEV)
@@ -38,7 +40,7 @@ def test_split_counts_small(splits):
     rows = np.arange(w.Nq)
     o_ref, l_ref = oracle_rows(q, k, v, oidx, ocnt, w.P, rows)
     assert_close(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16",
-                 f"split small, {splits} parts")
+                 f"split small, {splits} parts, D={D}")
 
 
 def test_split_ar_chunk_four_parts():
