@@ -285,8 +285,8 @@ def main() -> int:
                          "kernel for scaling HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported; this build "
-              "has no multi-GPU path (the sharding design is described in DESIGN.md).",
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported; the library "
+              "has no multi-GPU path (heads are independent, so it would shard by head).",
               file=sys.stderr)
         return 2
 
