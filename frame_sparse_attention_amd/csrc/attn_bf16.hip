@@ -133,6 +133,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char s_v[2][VBYTES];
   __shared__ int s_lo[FSA_MAX_CAP], s_hi[FSA_MAX_CAP];
   __shared__ int s_nruns[2];
+  __shared__ int s_order[128];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -145,6 +146,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
   tile /= splits;
   const int tq = tile % Tq;
   tile /= Tq;
+  // tile is now the head slot b * H + h; small grids visit heads in a
+  // cost-balanced order (at most 64 heads, at most 1024 blocks)
+  const int G = (int)(gridDim.x / ((unsigned)qtiles * splits * Tq));
+  if (gridDim.x <= 1024 && G <= 64)
+    tile = balanced_head(tile, G, Tq, la.cnt, la.cap, DUAL ? lb.cnt : nullptr, lb.cap, s_order);
   const int h = tile % H;
   const int b = tile / H;
   const long long head = (long long)b * H + h;

@@ -65,4 +65,47 @@ __device__ inline int xcd_logical_tile(int bid, int nblk) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Head order for small grids.  The contiguous per-XCD tile ranges hold whole
+// heads in turn, so when heads differ in cost (per-head policies: local,
+// anchor and memory heads) the XCDs finish at different times.  Heads are
+// ranked by cost, heaviest first (ties by index), and dealt from both ends of
+// that ranking -- heaviest, lightest, second heaviest, ... -- so each XCD range
+// pairs heavy heads with light ones.  Equal costs keep the plain order.  The
+// cost of a head is the number of frames its query frames list (list B
+// included).  Every block computes the same permutation; `s_tmp` is 128 LDS
+// ints; returns the head placed at position `slot`.
+__device__ inline int balanced_head(int slot, int G, int Tq, const int32_t *cnt_a, int cap_a,
+                                    const int32_t *cnt_b, int cap_b, int *s_tmp) {
+  const int l = threadIdx.x;
+  if (l < 64) {
+    int c = 0;
+    if (l < G) {
+      for (int t = 0; t < Tq; ++t) {
+        int n = cnt_a[(long long)l * Tq + t];
+        c += n < 0 ? 0 : (n > cap_a ? cap_a : n);
+        if (cnt_b != nullptr) {
+          n = cnt_b[(long long)l * Tq + t];
+          c += n < 0 ? 0 : (n > cap_b ? cap_b : n);
+        }
+      }
+    }
+    s_tmp[l] = c;
+  }
+  __syncthreads();
+  if (l < G) {
+    const int c = s_tmp[l], c0 = s_tmp[0];
+    int rank = 0;
+    bool equal = true;
+    for (int j = 0; j < G; ++j) {
+      const int cj = s_tmp[j];
+      rank += (cj > c || (cj == c && j < l)) ? 1 : 0;
+      equal = equal && cj == c0;
+    }
+    const int pos = equal ? l : (rank < (G + 1) / 2 ? 2 * rank : 2 * (G - 1 - rank) + 1);
+    s_tmp[64 + pos] = l;
+  }
+  __syncthreads();
+  return s_tmp[64 + slot];
+}
+
 }  // namespace fsa

@@ -209,6 +209,35 @@ def test_dual_pass_edges(D, P):
     assert_close(oab.cpu().numpy(), lab.cpu().numpy(), *ru, "bf16", f"dual O_AB D={D}")
 
 
+@pytest.mark.parametrize("B,H,widths", [(1, 5, [0, 3, 1, 5, 2]), (2, 3, [4, 0, 2, 1, 5, 3]),
+                                         (1, 4, [2, 2, 2, 2])])
+def test_small_grids_visit_heads_in_cost_order(B, H, widths):
+    # Grids this small reorder the heads by cost inside the kernel (heaviest,
+    # lightest, second heaviest, ...; equal costs keep the plain order).  Head
+    # (b, h) lists the frames [t - w, t] of query frame t with its own width w,
+    # so the heads' costs differ; every row of every head is checked.
+    P, T, D = 40, 6, 128
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s, outliers=2) for s in (61, 62, 63))
+    lists = [[[list(range(max(0, t - widths[b * H + h]), t + 1)) for t in range(T)]
+              for h in range(H)] for b in range(B)]
+    idx, cnt = _lists_to_arrays(lists, B, H)
+    _run_and_check(q, k, v, idx, cnt, P, "bf16", f"heads in cost order, B={B} H={H}")
+    # the dual pass takes list B into the cost: A = the own frame, B = the rest
+    la = [[[[t] for t in range(T)] for _ in range(H)] for _ in range(B)]
+    lb = [[[a[:-1] for a in lists[b][h]] for h in range(H)] for b in range(B)]
+    ia, ca = _lists_to_arrays(la, B, H)
+    ib, cb = _lists_to_arrays(lb, B, H)
+    prep = fsa.prepare_values(v.to(DEV))
+    oa, l_a, oab, l_ab = fsa.sparse_frame_attn_dual(q.to(DEV), k.to(DEV), prep, ia.to(DEV),
+                                                     ca.to(DEV), ib.to(DEV), cb.to(DEV), P)
+    torch.cuda.synchronize()
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    ra = oatt.sparse_frame_attention(qn, kn, vn, ia.numpy(), ca.numpy(), P)
+    ru = oatt.sparse_frame_attention(qn, kn, vn, idx.numpy(), cnt.numpy(), P)
+    assert_close(oa.cpu().numpy(), l_a.cpu().numpy(), *ra, "bf16", f"cost order dual O_A B={B}")
+    assert_close(oab.cpu().numpy(), l_ab.cpu().numpy(), *ru, "bf16", f"cost order dual O_AB B={B}")
+
+
 @pytest.mark.parametrize("kind,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
 def test_maximum_list_length_and_run_count(kind, D):
     # lists at the capacity limit (FSA_MAX_CAP = 1024 entries), a list of 512
