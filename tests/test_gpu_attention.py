@@ -210,12 +210,14 @@ def test_dual_pass_edges(D, P):
 
 
 @pytest.mark.parametrize("B,H,widths", [(1, 5, [0, 3, 1, 5, 2]), (2, 3, [4, 0, 2, 1, 5, 3]),
-                                         (1, 4, [2, 2, 2, 2])])
+                                         (1, 4, [2, 2, 2, 2]),
+                                         (2, 32, [(7 * i) % 6 for i in range(64)])])
 def test_small_grids_visit_heads_in_cost_order(B, H, widths):
     # Grids this small reorder the heads by cost inside the kernel (heaviest,
     # lightest, second heaviest, ...; equal costs keep the plain order).  Head
     # (b, h) lists the frames [t - w, t] of query frame t with its own width w,
-    # so the heads' costs differ; every row of every head is checked.
+    # so the heads' costs differ; every row of every head is checked.  The last
+    # case has 64 heads, the largest count that is reordered (384 blocks).
     P, T, D = 40, 6, 128
     q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s, outliers=2) for s in (61, 62, 63))
     lists = [[[list(range(max(0, t - widths[b * H + h]), t + 1)) for t in range(T)]
