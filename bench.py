@@ -64,8 +64,40 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float):
-    """The oracle on whole query frames of step 0 until `budget_s` seconds pass."""
+def host_cpu() -> dict:
+    """The host's CPU model, physical cores and the CPUs this process may use."""
+    model, cores = "unknown", set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model == "unknown":
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "physical_cores": len(cores) or None,
+            "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float, o_gpu=None, lse_gpu=None):
+    """The oracle on whole query frames of step 0 until `budget_s` seconds pass.
+    With the GPU's step-0 output (o_gpu, lse_gpu: CPU tensors [B,H,Nq,D] and
+    [B,H,Nq]) the same frames are also compared with it element by element."""
     import numpy as np
 
     from oracle import attention as oatt
@@ -79,10 +111,12 @@ def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float):
                                                rng.integers(0, w.Tq, 10_000))]
     done_pairs = 0
     frames = 0
-    t0 = time.perf_counter()
+    max_do = max_dl = 0.0
+    elapsed = 0.0
     kh_cache = {}
-    while frames < 2 or time.perf_counter() - t0 < budget_s:
+    while frames < 2 or elapsed < budget_s:
         h, t = order[frames]
+        t0 = time.perf_counter()
         if h not in kh_cache:
             kh_cache.clear()
             kh_cache[h] = (k[0, h].float().numpy(), v[0, h].float().numpy())
@@ -90,15 +124,58 @@ def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float):
         qh = q[0, h, t * w.P:(t + 1) * w.P].float().numpy()
         lst = idx[0, h, t, :cnt[0, h, t]]
         mask = oatt.token_mask(lst, w.Tk, w.P)
-        oatt.attend_rows(qh, kk, vv, mask, 1.0 / np.sqrt(w.D))
+        o_ref, l_ref = oatt.attend_rows(qh, kk, vv, mask, 1.0 / np.sqrt(w.D))
+        elapsed += time.perf_counter() - t0
         done_pairs += w.P * int(mask.sum())
         frames += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(4 * w.D * done_pairs / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"{frames} whole query frames (head, frame) of step 0, "
-                      f"{w.P} rows x {int(cnt[0, 0, 0]) * w.P} keys each, float64 numpy, "
-                      f"{dt:.1f} s"}
+        if o_gpu is not None:
+            rows = slice(t * w.P, (t + 1) * w.P)
+            max_do = max(max_do, float(np.max(np.abs(o_gpu[0, h, rows].numpy() - o_ref))))
+            max_dl = max(max_dl, float(np.max(np.abs(lse_gpu[0, h, rows].numpy() - l_ref))))
+    out = {"value": round(4 * w.D * done_pairs / elapsed / 1e12, 6), "unit": "TFLOP/s",
+           "cores": int(threads), "kind": "oracle",
+           "sample": f"{frames} whole query frames (head, frame) of step 0, "
+                     f"{w.P} rows x {int(cnt[0, 0, 0]) * w.P} keys each, float64 numpy, "
+                     f"{elapsed:.1f} s",
+           "host": host_cpu()}
+    if o_gpu is not None:
+        out["parity_vs_timed_output"] = {
+            "frames": frames, "rows": frames * w.P, "max_abs_dO": max_do, "max_abs_dLSE": max_dl,
+            "tolerance": {"dO": 1e-2, "dLSE": 1e-3},
+            "ok": bool(max_do <= 1e-2 and max_dl <= 1e-3)}
+    return out
+
+
+def issued_mfma(idx, cnt, P: int, D: int, rows_per_wave: int = 32, tile_keys: int = 64) -> int:
+    """32x32x16 MFMA instructions the attention kernel issues for frame lists
+    idx/cnt (numpy, [B,H,Tq,cap] / [B,H,Tq]) with one block per 128-row tile of
+    a query frame: every wavefront whose first row lies inside the frame
+    (ceil(P/32) of them per frame) walks every 64-key tile of every run of
+    consecutive listed frames (a run starts on the 8-key boundary at or below
+    its first key) and issues D/16 x 2 Q.K^T and D/32 x 4 P.V MFMAs per tile,
+    plus the Q.K^T of one tile past the last (computed, never used)."""
+    waves = -(-P // rows_per_wave)
+    qk, pv = 2 * (D // 16), 4 * (D // 32)
+    total = 0
+    B, H, Tq, _ = idx.shape
+    for b in range(B):
+        for h in range(H):
+            for t in range(Tq):
+                lst = idx[b, h, t, :cnt[b, h, t]]
+                if lst.size == 0:
+                    continue
+                tiles = 0
+                start = prev = int(lst[0])
+                for f in list(lst[1:].tolist()) + [None]:
+                    if f is not None and f == prev + 1:
+                        prev = f
+                        continue
+                    lo = (start * P) & ~7
+                    tiles += -(-((prev + 1) * P - lo) // tile_keys)
+                    if f is not None:
+                        start = prev = f
+                total += waves * (tiles * (qk + pv) + qk)
+    return int(total)
 
 
 def time_ms(fn, reps: int = 20) -> float:
@@ -375,8 +452,13 @@ def main() -> int:
     value = flop_per_step / (ms_per_step * 1e-3) / 1e12
     achieved = flop_per_step / (attn_ms * 1e-3) / 1e12
     traffic = measured_traffic()
-    qtiles = -(-w.P // 128)
-    issued_pairs = w.B * w.H * w.Tq * qtiles * 128 * int(cnt[0, 0, 0].item()) * w.P
+    # work the kernel issues for the lists of the steps just timed (one launch per step)
+    n_mfma = []
+    for s in range(w.steps):
+        run_step(s)
+        torch.cuda.synchronize()
+        n_mfma.append(issued_mfma(idx.cpu().numpy(), cnt.cpu().numpy(), w.P, w.D))
+    issued_per_launch = sum(n_mfma[i % w.steps] for i in range(args.steps)) / args.steps
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -399,7 +481,10 @@ def main() -> int:
         "kernels_ms": {"build_frame_sets": round(build_ms, 4),
                        "prepare_values": round(prep_ms, 4),
                        "sparse_frame_attn": round(attn_ms, 4)},
-        "issued_tile_tflops": round(4 * w.D * issued_pairs / (attn_ms * 1e-3) / 1e12, 3),
+        "issued": {"mfma_32x32x16_per_launch": int(round(issued_per_launch)),
+                   "flop_per_launch": int(round(issued_per_launch)) * 32768,
+                   "over_algorithmic": round(issued_per_launch * 32768 / flop_per_step, 4),
+                   "tflops": round(issued_per_launch * 32768 / (attn_ms * 1e-3) / 1e12, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
@@ -415,7 +500,8 @@ def main() -> int:
         run_step(0)
         torch.cuda.synchronize()
         idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, idx_h, cnt_h, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, idx_h, cnt_h, args.cpu_seconds,
+                                           o.cpu(), lse.cpu())
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

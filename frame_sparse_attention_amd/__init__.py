@@ -1,9 +1,11 @@
 """Python binding of libfsa (frame-block-sparse softmax attention on MI355X).
 
-A thin ctypes layer over the C ABI declared in include/fsa.h: it checks
-tensor dtypes/shapes, allocates outputs and workspaces with torch on the
-inputs' device, passes raw pointers and torch's current HIP stream, and turns
-a non-OK status into FsaError.  Every computation happens in the library's HIP
+A thin ctypes layer over the C ABI declared in include/fsa.h: it checks that
+every tensor handed to a device call is a contiguous tensor on the inputs' GPU
+with the dtype and shape the call expects (before anything is launched),
+allocates outputs and workspaces with torch on that device, passes raw
+pointers and torch's current HIP stream, and turns a non-OK status into
+FsaError.  Every computation happens in the library's HIP
 kernels; there is no fallback.  The first library call raises ImportError
 when libfsa.so has not been built (python -m frame_sparse_attention_amd.build);
 the library is loaded lazily so that the build script in this package can
@@ -163,18 +165,87 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
-def _need_contig(*ts):
-    for t in ts:
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+def _on_gpu(**named) -> torch.device:
+    """Checks the tensors handed to a device call: each one given (None is
+    skipped) must be a contiguous torch tensor on one and the same GPU.
+    Returns that device.  Raises before any pointer reaches a kernel."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not torch.is_tensor(t):
+            raise TypeError(f"{name} must be a torch tensor, not {type(t).__name__}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}: the kernels read and write GPU memory "
+                             "only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if dev is None:
+        raise ValueError("no GPU tensor given")
+    return dev
+
+
+def _expect(t, name: str, dtype=None, shape=None) -> None:
+    """Dtype and exact shape of a tensor (None: not given, nothing to check)."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _qk_shapes(q: torch.Tensor, k: torch.Tensor):
+    """(B, H, Nq, Nk, D) of q [B,H,Nq,D] and k [B,H,Nk,D] of one dtype."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, D]")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    _expect(k, "k", q.dtype, (B, H, Nk, D))
+    _dtype_code(q)
+    return B, H, Nq, Nk, D
+
+
+def _lists(idx, cnt, B: int, H: int, rows: int, name: str = "idx"):
+    """Frame lists idx int32 [B, H, rows, cap] and cnt int32 [B, H, rows]; returns cap."""
+    if idx.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, {rows}, cap]")
+    _expect(idx, name, torch.int32, (B, H, rows, idx.shape[3]))
+    _expect(cnt, "cnt" if name == "idx" else name.replace("idx", "cnt"), torch.int32,
+            (B, H, rows))
+    return idx.shape[3]
+
+
+def _outputs(dev, B: int, H: int, Nq: int, D: int, out, out_lse):
+    """O float32 [B,H,Nq,D] and LSE float32 [B,H,Nq]: the given ones (checked) or new."""
+    _expect(out, "out", torch.float32, (B, H, Nq, D))
+    _expect(out_lse, "out_lse", torch.float32, (B, H, Nq))
+    o = out if out is not None else torch.empty((B, H, Nq, D), dtype=torch.float32, device=dev)
+    lse = out_lse if out_lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
+                                                          device=dev)
+    return o, lse
+
+
+def _frames(N: int, P: int) -> int:
+    if P <= 0 or N % P:
+        raise ValueError(f"N={N} is not a positive multiple of P={P}")
+    return N // P
 
 
 # ----------------------------------------------------------------------------- frame sets
 def frame_set_capacity(policies, Tq: int, Tk: int, offset: int = 0, chunk: int = 1) -> int:
     """Smallest cap that holds every frame set the policies can produce."""
     out = ctypes.c_int32(0)
-    _check(_load().fsa_frame_set_capacity(len(policies), _policies(policies), Tq, Tk, offset, chunk,
-                                       ctypes.byref(out)))
+    _check(_load().fsa_frame_set_capacity(len(policies), _policies(policies), Tq, Tk, offset,
+                                          chunk, ctypes.byref(out)))
     return out.value
 
 
@@ -186,19 +257,24 @@ def build_frame_sets(policies, B: int, Tq: int, Tk: int, offset: int = 0, chunk:
     selected: device int32 [B, H, Tq // chunk, k] frames chosen per query group
     (read for MEMORY heads only)."""
     H = len(policies)
+    device = torch.device(device)
+    if device.type != "cuda":
+        raise ValueError(f"device {device}: frame sets are built by a GPU kernel "
+                         "(build_frame_sets_host builds them on the CPU)")
     if cap is None:
         cap = frame_set_capacity(policies, Tq, Tk, offset, chunk)
-    idx = torch.empty((B, H, Tq, cap), dtype=torch.int32, device=device)
-    cnt = torch.empty((B, H, Tq), dtype=torch.int32, device=device)
     topk_k = 0
     if selected is not None:
-        if selected.dtype != torch.int32 or selected.dim() != 4:
-            raise ValueError("selected must be int32 [B, H, groups, k]")
-        _need_contig(selected)
+        if selected.dim() != 4 or chunk <= 0:
+            raise ValueError("selected must be int32 [B, H, Tq // chunk, k]")
+        device = _on_gpu(selected=selected)
+        _expect(selected, "selected", torch.int32, (B, H, Tq // chunk, selected.shape[3]))
         topk_k = selected.shape[3]
+    idx = torch.empty((B, H, Tq, cap), dtype=torch.int32, device=device)
+    cnt = torch.empty((B, H, Tq), dtype=torch.int32, device=device)
     _check(_load().fsa_build_frame_sets(B, H, Tq, Tk, offset, chunk, _policies(policies),
-                                     _ptr(selected), topk_k, cap, _ptr(idx), _ptr(cnt),
-                                     _stream(idx.device)))
+                                        _ptr(selected), topk_k, cap, _ptr(idx), _ptr(cnt),
+                                        _stream(idx.device)))
     return idx, cnt
 
 
@@ -212,10 +288,14 @@ def build_frame_sets_host(policies, B: int, Tq: int, Tk: int, offset: int = 0, c
     cnt = np.empty((B, H, Tq), dtype=np.int32)
     topk_k = 0
     if selected is not None:
+        if torch.is_tensor(selected):
+            selected = selected.cpu().numpy()
         selected = np.ascontiguousarray(selected, dtype=np.int32)
+        if selected.ndim != 4 or chunk <= 0 or selected.shape[:3] != (B, H, Tq // chunk):
+            raise ValueError("selected must be int32 [B, H, Tq // chunk, k]")
         topk_k = selected.shape[3]
     _check(_load().fsa_build_frame_sets_host(B, H, Tq, Tk, offset, chunk, _policies(policies),
-                                          _ptr(selected), topk_k, cap, _ptr(idx), _ptr(cnt)))
+                                             _ptr(selected), topk_k, cap, _ptr(idx), _ptr(cnt)))
     return idx, cnt
 
 
@@ -223,11 +303,31 @@ def validate_frame_sets(idx, cnt, Tk: int) -> None:
     """Raises FsaError (FSA_E_LIST) unless every list is sorted, unique and in range."""
     idx = np.ascontiguousarray(idx.cpu().numpy() if torch.is_tensor(idx) else idx, dtype=np.int32)
     cnt = np.ascontiguousarray(cnt.cpu().numpy() if torch.is_tensor(cnt) else cnt, dtype=np.int32)
+    if idx.ndim != 4 or cnt.shape != idx.shape[:3]:
+        raise ValueError("idx must be [B, H, Tq, cap] and cnt [B, H, Tq]")
     B, H, Tq, cap = idx.shape
     _check(_load().fsa_validate_frame_sets(B, H, Tq, Tk, cap, _ptr(idx), _ptr(cnt)))
 
 
 # ----------------------------------------------------------------------------- top-k
+def select_topk_workspace_size(B: int, H: int, Nq: int, D: int, P: int, q_group: int,
+                               cand_begin: int, cand_end: int) -> int:
+    nbytes = ctypes.c_size_t(0)
+    _check(_load().fsa_select_topk_workspace_size(B, H, Nq, D, P, q_group, cand_begin, cand_end,
+                                                  ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def _topk_outputs(dev, B, H, G, topk, F, out, return_scores):
+    _expect(out, "out", torch.int32, (B, H, G, topk))
+    if out is None:
+        out = torch.full((B, H, G, topk), -1, dtype=torch.int32, device=dev)
+    scores = None
+    if return_scores:
+        scores = torch.full((B, H, G, F), float("nan"), dtype=torch.float64, device=dev)
+    return out, scores
+
+
 def select_topk_frames(q: torch.Tensor, k: torch.Tensor, P: int, h_begin: int, h_end: int,
                        q_group: int, cand_begin: int, cand_end: int, topk: int,
                        return_scores: bool = False, out: torch.Tensor | None = None):
@@ -235,24 +335,16 @@ def select_topk_frames(q: torch.Tensor, k: torch.Tensor, P: int, h_begin: int, h
 
     Returns int32 [B, H, G, topk] (rows of other heads are -1, or left as in
     `out`), and float64 scores [B, H, G, cand_end - cand_begin] when asked."""
-    _need_contig(q, k)
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
+    dev = _on_gpu(q=q, k=k, out=out)
+    B, H, Nq, Nk, D = _qk_shapes(q, k)
     G = Nq // (q_group * P) if q_group * P > 0 else 0
-    if out is None:
-        out = torch.full((B, H, G, topk), -1, dtype=torch.int32, device=q.device)
-    scores = None
-    if return_scores:
-        scores = torch.full((B, H, G, cand_end - cand_begin), float("nan"), dtype=torch.float64,
-                            device=q.device)
-    nbytes = ctypes.c_size_t(0)
-    _check(_load().fsa_select_topk_workspace_size(B, H, Nq, D, P, q_group, cand_begin, cand_end,
-                                               ctypes.byref(nbytes)))
-    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)
+    out, scores = _topk_outputs(dev, B, H, G, topk, cand_end - cand_begin, out, return_scores)
+    nbytes = select_topk_workspace_size(B, H, Nq, D, P, q_group, cand_begin, cand_end)
+    ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev)
     _check(_load().fsa_select_topk_frames(_ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P,
-                                       h_begin, h_end, q_group, cand_begin, cand_end, topk,
-                                       _ptr(out), _ptr(scores), _ptr(ws), nbytes.value,
-                                       _stream(q.device)))
+                                          h_begin, h_end, q_group, cand_begin, cand_end, topk,
+                                          _ptr(out), _ptr(scores), _ptr(ws), nbytes,
+                                          _stream(dev)))
     return (out, scores) if return_scores else out
 
 
@@ -266,9 +358,8 @@ def select_hsa_blocks(q: torch.Tensor, k: torch.Tensor, P: int, block: int, h_be
     frame) into idx [B, H, Nq // block, cap] and cnt [B, H, Nq // block]
     (allocated with -1 / 0 when not given; rows of other heads are left as
     they are) and returns (idx, cnt).  Attend with P = block."""
-    _need_contig(q, k)
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
+    dev = _on_gpu(q=q, k=k, idx=idx, cnt=cnt)
+    B, H, Nq, Nk, D = _qk_shapes(q, k)
     if block <= 0:
         raise ValueError("block must be positive")
     nb = P // block if P % block == 0 else 0
@@ -276,22 +367,19 @@ def select_hsa_blocks(q: torch.Tensor, k: torch.Tensor, P: int, block: int, h_be
         cap = topk_blocks + n_recent * nb if idx is None else idx.shape[3]
     G = Nq // block
     if idx is None:
-        idx = torch.full((B, H, G, cap), -1, dtype=torch.int32, device=q.device)
+        idx = torch.full((B, H, G, cap), -1, dtype=torch.int32, device=dev)
     if cnt is None:
-        cnt = torch.zeros((B, H, G), dtype=torch.int32, device=q.device)
-    _need_contig(idx, cnt)
-    if idx.dtype != torch.int32 or cnt.dtype != torch.int32:
-        raise TypeError("idx and cnt must be int32")
-    if idx.shape != (B, H, G, cap) or cnt.shape != (B, H, G):
-        raise ValueError("idx must be [B, H, Nq // block, cap] and cnt [B, H, Nq // block]")
+        cnt = torch.zeros((B, H, G), dtype=torch.int32, device=dev)
+    _expect(idx, "idx", torch.int32, (B, H, G, cap))
+    _expect(cnt, "cnt", torch.int32, (B, H, G))
     nbytes = ctypes.c_size_t(0)
     _check(_load().fsa_select_hsa_workspace_size(B, H, Nq, Nk, D, P, block, offset, chunk,
-                                              h_begin, h_end, n_recent, ctypes.byref(nbytes)))
-    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)
+                                                 h_begin, h_end, n_recent, ctypes.byref(nbytes)))
+    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
     _check(_load().fsa_select_hsa_blocks(_ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P,
-                                      block, offset, chunk, h_begin, h_end, n_recent,
-                                      topk_frames, topk_blocks, cap, _ptr(idx), _ptr(cnt),
-                                      _ptr(ws), nbytes.value, _stream(q.device)))
+                                         block, offset, chunk, h_begin, h_end, n_recent,
+                                         topk_frames, topk_blocks, cap, _ptr(idx), _ptr(cnt),
+                                         _ptr(ws), nbytes.value, _stream(dev)))
     return idx, cnt
 
 
@@ -311,7 +399,7 @@ def cag_schedule(cost, s_target: float, s_base: float, s_max: float, candidates=
         bud = np.empty(n, dtype=np.int32)
     beta = ctypes.c_double(0.0)
     _check(_load().fsa_cag_schedule(n, _ptr(cost), float(s_target), float(s_base), float(s_max),
-                                 _ptr(cand), _ptr(sp), _ptr(bud), ctypes.byref(beta)))
+                                    _ptr(cand), _ptr(sp), _ptr(bud), ctypes.byref(beta)))
     return sp, bud, beta.value
 
 
@@ -322,23 +410,21 @@ def rope_reencode(q: torch.Tensor, k: torch.Tensor, idx: torch.Tensor, cnt: torc
     idx int32 [B, H, cap], cnt int32 [B, H].  Returns (q_out, k_out); q_out has
     every row written, k_out only the rows of listed frames (a fresh k_out
     starts as a copy of k).  Either output may be its input (in place)."""
-    _need_contig(q, k, idx, cnt)
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, D) or k.dtype != q.dtype:
-        raise ValueError("k must be [B, H, Nk, D] with q's dtype")
-    if idx.dtype != torch.int32 or cnt.dtype != torch.int32:
-        raise TypeError("idx and cnt must be int32")
-    if idx.dim() != 3 or idx.shape[:2] != (B, H) or cnt.shape != (B, H):
+    _on_gpu(q=q, k=k, idx=idx, cnt=cnt, q_out=q_out, k_out=k_out)
+    B, H, Nq, Nk, D = _qk_shapes(q, k)
+    if idx.dim() != 3:
         raise ValueError("idx must be [B, H, cap] and cnt [B, H]")
+    _expect(idx, "idx", torch.int32, (B, H, idx.shape[2]))
+    _expect(cnt, "cnt", torch.int32, (B, H))
+    _expect(q_out, "q_out", q.dtype, q.shape)
+    _expect(k_out, "k_out", k.dtype, k.shape)
     if q_out is None:
         q_out = torch.empty_like(q)
     if k_out is None:
         k_out = k.clone()
-    _need_contig(q_out, k_out)
     _check(_load().fsa_rope_reencode(_ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P,
-                                  _ptr(idx), _ptr(cnt), idx.shape[2], offset, rot, float(base),
-                                  _ptr(q_out), _ptr(k_out), _stream(q.device)))
+                                     _ptr(idx), _ptr(cnt), idx.shape[2], offset, rot,
+                                     float(base), _ptr(q_out), _ptr(k_out), _stream(q.device)))
     return q_out, k_out
 
 
@@ -355,45 +441,36 @@ def sparse_frame_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: to
                       workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
                       out_lse: torch.Tensor | None = None):
     """Frame-sparse attention: returns (O float32 [B,H,Nq,D], LSE float32 [B,H,Nq])."""
-    _need_contig(q, k, v, idx, cnt)
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share one dtype")
-    if idx.dtype != torch.int32 or cnt.dtype != torch.int32:
-        raise TypeError("idx and cnt must be int32")
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
-        raise ValueError("k and v must be [B, H, Nk, D] matching q")
-    if idx.dim() != 4 or idx.shape[:2] != (B, H) or cnt.shape != idx.shape[:3]:
-        raise ValueError("idx must be [B,H,Tq,cap] and cnt [B,H,Tq]")
-    if P > 0 and idx.shape[2] != Nq // P:
-        raise ValueError("idx has the wrong number of query frames")
+    dev = _on_gpu(q=q, k=k, v=v, idx=idx, cnt=cnt, workspace=workspace, out=out,
+                  out_lse=out_lse)
+    B, H, Nq, Nk, D = _qk_shapes(q, k)
+    _expect(v, "v", q.dtype, (B, H, Nk, D))
+    cap = _lists(idx, cnt, B, H, _frames(Nq, P))
     dt = _dtype_code(q)
-    o = out if out is not None else torch.empty((B, H, Nq, D), dtype=torch.float32,
-                                                device=q.device)
-    lse = out_lse if out_lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
-                                                          device=q.device)
+    o, lse = _outputs(dev, B, H, Nq, D, out, out_lse)
     need = sparse_frame_attn_workspace_size(dt, B, H, Nk, D)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(_load().fsa_sparse_frame_attn(_ptr(q), _ptr(k), _ptr(v), dt, B, H, Nq, Nk, D, P,
-                                      _ptr(idx), _ptr(cnt), idx.shape[3],
-                                      float(scale) if scale is not None else 0.0, _ptr(o),
-                                      _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device)))
+                                         _ptr(idx), _ptr(cnt), cap,
+                                         float(scale) if scale is not None else 0.0, _ptr(o),
+                                         _ptr(lse), _ptr(workspace), _nbytes(workspace),
+                                         _stream(dev)))
     return o, lse
 
 
 def prepare_values(v: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """bf16 V [B,H,Nk,D] -> the float16 key-chunked transposed copy the attention
     reads (a uint8 buffer of sparse_frame_attn_workspace_size bytes)."""
-    _need_contig(v)
+    dev = _on_gpu(v=v, out=out)
+    if v.dim() != 4:
+        raise ValueError("v must be [B, H, Nk, D]")
     B, H, Nk, D = v.shape
     need = sparse_frame_attn_workspace_size(_dtype_code(v), B, H, Nk, D)
     if out is None:
-        out = torch.empty(max(1, need), dtype=torch.uint8, device=v.device)
+        out = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
     _check(_load().fsa_prepare_values(_ptr(v), _dtype_code(v), B, H, Nk, D, _ptr(out),
-                                   out.numel() * out.element_size(), _stream(v.device)))
+                                      _nbytes(out), _stream(dev)))
     return out
 
 
@@ -402,19 +479,14 @@ def sparse_frame_attn_prepared(q: torch.Tensor, k: torch.Tensor, prepared: torch
                                scale: float | None = None, out: torch.Tensor | None = None,
                                out_lse: torch.Tensor | None = None):
     """Attention reading values already converted by prepare_values."""
-    _need_contig(q, k, prepared, idx, cnt)
-    if q.dtype != k.dtype:
-        raise TypeError("q and k must share one dtype")
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    o = out if out is not None else torch.empty((B, H, Nq, D), dtype=torch.float32,
-                                                device=q.device)
-    lse = out_lse if out_lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
-                                                          device=q.device)
+    dev = _on_gpu(q=q, k=k, prepared=prepared, idx=idx, cnt=cnt, out=out, out_lse=out_lse)
+    B, H, Nq, Nk, D = _qk_shapes(q, k)
+    cap = _lists(idx, cnt, B, H, _frames(Nq, P))
+    o, lse = _outputs(dev, B, H, Nq, D, out, out_lse)
     _check(_load().fsa_sparse_frame_attn_prepared(
         _ptr(q), _ptr(k), _ptr(prepared), _dtype_code(q), B, H, Nq, Nk, D, P, _ptr(idx),
-        _ptr(cnt), idx.shape[3], float(scale) if scale is not None else 0.0, _ptr(o), _ptr(lse),
-        prepared.numel() * prepared.element_size(), _stream(q.device)))
+        _ptr(cnt), cap, float(scale) if scale is not None else 0.0, _ptr(o), _ptr(lse),
+        _nbytes(prepared), _stream(dev)))
     return o, lse
 
 
@@ -424,7 +496,7 @@ def attn_split_plan(B: int, H: int, Nq: int, D: int, P: int, splits: int = 0):
     n = ctypes.c_int32(0)
     nbytes = ctypes.c_size_t(0)
     _check(_load().fsa_attn_split_plan(B, H, Nq, D, P, splits, ctypes.byref(n),
-                                    ctypes.byref(nbytes)))
+                                       ctypes.byref(nbytes)))
     return n.value, nbytes.value
 
 
@@ -434,26 +506,18 @@ def sparse_frame_attn_split(q: torch.Tensor, k: torch.Tensor, prepared: torch.Te
                             out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None):
     """Attention with each frame list cut into `splits` parts (0: the library's
     choice for the grid) whose partials are merged through their LSE."""
-    _need_contig(q, k, prepared, idx, cnt)
-    if idx.dtype != torch.int32 or cnt.dtype != torch.int32:
-        raise TypeError("idx and cnt must be int32")
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    if idx.dim() != 4 or idx.shape[:2] != (B, H) or cnt.shape != idx.shape[:3]:
-        raise ValueError("idx must be [B,H,Tq,cap] and cnt [B,H,Tq]")
+    dev = _on_gpu(q=q, k=k, prepared=prepared, idx=idx, cnt=cnt, workspace=workspace, out=out,
+                  out_lse=out_lse)
+    B, H, Nq, Nk, D = _qk_shapes(q, k)
+    cap = _lists(idx, cnt, B, H, _frames(Nq, P))
     S, nbytes = attn_split_plan(B, H, Nq, D, P, splits)
-    o = out if out is not None else torch.empty((B, H, Nq, D), dtype=torch.float32,
-                                                device=q.device)
-    lse = out_lse if out_lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
-                                                          device=q.device)
+    o, lse = _outputs(dev, B, H, Nq, D, out, out_lse)
     if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _check(_load().fsa_sparse_frame_attn_prepared_split(
         _ptr(q), _ptr(k), _ptr(prepared), _dtype_code(q), B, H, Nq, Nk, D, P, _ptr(idx),
-        _ptr(cnt), idx.shape[3], 0.0 if scale is None else float(scale), S, _ptr(o), _ptr(lse),
-        prepared.numel() * prepared.element_size(), _ptr(workspace), ws_bytes,
-        _stream(q.device)))
+        _ptr(cnt), cap, 0.0 if scale is None else float(scale), S, _ptr(o), _ptr(lse),
+        _nbytes(prepared), _ptr(workspace), _nbytes(workspace), _stream(dev)))
     return o, lse
 
 
@@ -462,32 +526,38 @@ def sparse_frame_attn_dual(q: torch.Tensor, k: torch.Tensor, prepared: torch.Ten
                            cnt_b: torch.Tensor, P: int, scale: float | None = None):
     """One pass over frame lists A then B: returns (O_A, LSE_A, O_AB, LSE_AB),
     attention over A alone and over A and B together (disjoint lists)."""
-    _need_contig(q, k, prepared, idx_a, cnt_a, idx_b, cnt_b)
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    outs = [torch.empty((B, H, Nq, D), dtype=torch.float32, device=q.device) for _ in range(2)]
-    lses = [torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) for _ in range(2)]
+    dev = _on_gpu(q=q, k=k, prepared=prepared, idx_a=idx_a, cnt_a=cnt_a, idx_b=idx_b,
+                  cnt_b=cnt_b)
+    B, H, Nq, Nk, D = _qk_shapes(q, k)
+    Tq = _frames(Nq, P)
+    cap_a = _lists(idx_a, cnt_a, B, H, Tq, "idx_a")
+    cap_b = _lists(idx_b, cnt_b, B, H, Tq, "idx_b")
+    outs = [torch.empty((B, H, Nq, D), dtype=torch.float32, device=dev) for _ in range(2)]
+    lses = [torch.empty((B, H, Nq), dtype=torch.float32, device=dev) for _ in range(2)]
     _check(_load().fsa_sparse_frame_attn_dual_prepared(
         _ptr(q), _ptr(k), _ptr(prepared), _dtype_code(q), B, H, Nq, Nk, D, P, _ptr(idx_a),
-        _ptr(cnt_a), idx_a.shape[3], _ptr(idx_b), _ptr(cnt_b), idx_b.shape[3],
+        _ptr(cnt_a), cap_a, _ptr(idx_b), _ptr(cnt_b), cap_b,
         float(scale) if scale is not None else 0.0, _ptr(outs[0]), _ptr(lses[0]), _ptr(outs[1]),
-        _ptr(lses[1]), prepared.numel() * prepared.element_size(), _stream(q.device)))
+        _ptr(lses[1]), _nbytes(prepared), _stream(dev)))
     return outs[0], lses[0], outs[1], lses[1]
 
 
 def merge_lse(o1: torch.Tensor, lse1: torch.Tensor, o2: torch.Tensor, lse2: torch.Tensor,
               out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None):
     """Exact LSE merge of two partial attentions (float32); returns (O, LSE)."""
-    _need_contig(o1, lse1, o2, lse2)
-    if o1.shape != o2.shape or lse1.shape != lse2.shape or o1.shape[:-1] != lse1.shape:
-        raise ValueError("o1/o2 must be [..., D] and lse1/lse2 the matching [...]")
-    for t in (o1, lse1, o2, lse2):
-        if t.dtype != torch.float32:
-            raise TypeError("merge_lse works on float32 tensors")
+    _on_gpu(o1=o1, lse1=lse1, o2=o2, lse2=lse2, out=out, out_lse=out_lse)
+    if o1.dim() < 1 or o1.shape[:-1] != lse1.shape:
+        raise ValueError("o1 must be [..., D] and lse1 the matching [...]")
+    _expect(o1, "o1", torch.float32)
+    _expect(lse1, "lse1", torch.float32)
+    _expect(o2, "o2", torch.float32, o1.shape)
+    _expect(lse2, "lse2", torch.float32, lse1.shape)
+    _expect(out, "out", torch.float32, o1.shape)
+    _expect(out_lse, "out_lse", torch.float32, lse1.shape)
     D = o1.shape[-1]
     rows = lse1.numel()
     o = out if out is not None else torch.empty_like(o1)
     lse = out_lse if out_lse is not None else torch.empty_like(lse1)
     _check(_load().fsa_merge_lse(_ptr(o1), _ptr(lse1), _ptr(o2), _ptr(lse2), rows, D, _ptr(o),
-                              _ptr(lse), _stream(o1.device)))
+                                 _ptr(lse), _stream(o1.device)))
     return o, lse

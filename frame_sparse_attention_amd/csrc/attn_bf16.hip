@@ -48,6 +48,15 @@ constexpr int kWaitVm0 = 0x0F70;
 // One block per (head, 64 keys): 16-byte coalesced loads of the [64][D] bf16
 // tile, conversion to float16 into LDS, then 16-byte coalesced stores of the
 // [8 chunks][D][8] image (HBM-bound: 2 bytes read + 2 written per element).
+//
+// Values beyond the float16 range saturate to +-65504 instead of becoming
+// infinite: a 64-key tile also holds keys outside a row's frame set (before
+// an unaligned run start, after a run end), whose probabilities are exactly
+// 0, and 0 * inf would turn that row's output into NaN.  NaN stays NaN.
+__device__ inline _Float16 f16_saturate(float x) {
+  const float c = fminf(fmaxf(x, -65504.f), 65504.f);
+  return (_Float16)(x != x ? x : c);
+}
 template <int D>
 __global__ void __launch_bounds__(256) v_to_f16_chunked_kernel(const uint16_t *__restrict__ v,
                                                                _Float16 *__restrict__ vt,
@@ -64,8 +73,8 @@ __global__ void __launch_bounds__(256) v_to_f16_chunked_kernel(const uint16_t *_
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      tile[kk][c * 8 + 2 * e] = (_Float16)__uint_as_float(w[e] << 16);
-      tile[kk][c * 8 + 2 * e + 1] = (_Float16)__uint_as_float(w[e] & 0xffff0000u);
+      tile[kk][c * 8 + 2 * e] = f16_saturate(__uint_as_float(w[e] << 16));
+      tile[kk][c * 8 + 2 * e + 1] = f16_saturate(__uint_as_float(w[e] & 0xffff0000u));
     }
   }
   __syncthreads();

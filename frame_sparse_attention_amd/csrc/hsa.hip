@@ -42,6 +42,10 @@ __global__ void __launch_bounds__(kPoolThreads) hsa_frame_sums_kernel(
   (void)Fc;
 }
 
+// A NaN score (from non-finite inputs) ranks as -inf, so (score, index) stays
+// a strict total order and exactly k candidates are kept.
+__device__ inline double nan_last(double s) { return s != s ? -INFINITY : s; }
+
 // (score, index) order: higher score first, then lower index.
 __device__ inline bool hsa_better(double s1, int i1, double s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
@@ -130,12 +134,14 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   // level 1: frames
   const double *kf_base = kframe + bh * Fc * D;
   for (int f = lane; f < first_recent; f += 64) {
-    s_score[f] = ordered_dot(qs, kf_base + (long long)f * D, D);
+    s_score[f] = nan_last(ordered_dot(qs, kf_base + (long long)f * D, D));
     s_taken[f] = 0;
   }
   __syncthreads();
   take_best(s_score, s_taken, first_recent, kf);
-  compact_taken(s_taken, first_recent, [&](int pos, int f) { s_frames[pos] = f; });
+  compact_taken(s_taken, first_recent, [&](int pos, int f) {
+    if (pos < kf) s_frames[pos] = f;
+  });
   __syncthreads();
 
   // level 2: blocks of the chosen frames; candidate c is block
@@ -144,7 +150,7 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   const double *kb_base = kblk + bh * (long long)Fc * nb * D;
   for (int c = lane; c < nbc; c += 64) {
     const long long blk = (long long)s_frames[c / nb] * nb + c % nb;
-    s_score[c] = ordered_dot(qs, kb_base + blk * D, D);
+    s_score[c] = nan_last(ordered_dot(qs, kb_base + blk * D, D));
     s_taken[c] = 0;
   }
   __syncthreads();
@@ -152,7 +158,9 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
 
   const long long row = ((long long)b * H + h_begin + hs) * Gq + j;
   int32_t *out = idx + row * cap;
-  compact_taken(s_taken, nbc, [&](int pos, int c) { out[pos] = s_frames[c / nb] * nb + c % nb; });
+  compact_taken(s_taken, nbc, [&](int pos, int c) {
+    if (pos < kb) out[pos] = s_frames[c / nb] * nb + c % nb;
+  });
   const int n_rec = n_recent * nb;
   for (int r = lane; r < n_rec; r += 64) out[kb + r] = first_recent * nb + r;
   for (int p = kb + n_rec + lane; p < cap; p += 64) out[p] = -1;

@@ -52,7 +52,9 @@ __global__ void __launch_bounds__(64) score_select_kernel(
   const long long out_head = (long long)b * H + h_begin + hs;
   for (int fi = lane; fi < F; fi += 64) {
     const double acc = ordered_dot(qs, ks + (long long)fi * D, D);
-    s_score[fi] = acc;
+    // a NaN score (from non-finite inputs) ranks as -inf, so (score, frame)
+    // stays a strict total order and exactly topk frames are kept
+    s_score[fi] = acc != acc ? -INFINITY : acc;
     s_taken[fi] = 0;
     if (out_scores) out_scores[(out_head * G + g) * F + fi] = acc;
   }
@@ -74,7 +76,8 @@ __global__ void __launch_bounds__(64) score_select_kernel(
       const int fi = base + lane;
       const bool keep = fi < F && s_taken[fi];
       const unsigned long long mask = __ballot(keep);
-      if (keep) out[count + __popcll(mask & ((1ull << lane) - 1ull))] = cand_begin + fi;
+      const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+      if (keep && pos < topk) out[pos] = cand_begin + fi;
       count += __popcll(mask);
     }
     return;

@@ -190,7 +190,9 @@ fsa_status fsa_validate_frame_sets(int32_t B, int32_t H, int32_t Tq, int32_t Tk,
  * candidates outside [0, Tk) or more than 4096 of them, q_group does not
  * divide Tq, bad head range), FSA_E_SHAPE (D outside [1, 256], ...),
  * FSA_E_DTYPE, FSA_E_CAPACITY (workspace), FSA_E_HIP.
- * Non-finite inputs give unspecified frames (a precondition). */
+ * Non-finite inputs give unspecified frames (a precondition); a NaN score
+ * ranks below every number, so each row still receives exactly topk_k
+ * distinct candidate frames and nothing outside out_frames is written. */
 fsa_status fsa_select_topk_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t D,
                                           int32_t P, int32_t q_group, int32_t cand_begin,
                                           int32_t cand_end, size_t *bytes);
@@ -262,7 +264,9 @@ fsa_status fsa_cag_schedule(int32_t n_chunks, const double *cost, double s_targe
  * outside [1, 256]; P not a multiple of block; Nq or Nk not a multiple of P),
  * FSA_E_DTYPE, FSA_E_CAPACITY (cap below topk_blocks + n_recent*nb or above
  * FSA_MAX_CAP; workspace), FSA_E_HIP.  Non-finite inputs give unspecified
- * blocks (a precondition). */
+ * blocks (a precondition); a NaN score ranks below every number, so each row
+ * still holds exactly topk_blocks chosen blocks and nothing past its cap is
+ * written. */
 fsa_status fsa_select_hsa_workspace_size(int32_t B, int32_t H, int32_t Nq, int32_t Nk, int32_t D,
                                          int32_t P, int32_t block, int32_t q_kv_offset,
                                          int32_t chunk, int32_t h_begin, int32_t h_end,
@@ -322,6 +326,12 @@ fsa_status fsa_rope_reencode(const void *q, const void *k, int32_t dt, int32_t B
  * its row sums in float32, and forms P.V with float16 MFMA on float16
  * probabilities and float16 values (float32 accumulation); O and LSE are
  * float32.
+ * Value range (bf16 path): values are used as float16, so attended values
+ * must satisfy |v| <= 65504 (a precondition); larger finite values and
+ * infinities are saturated to +-65504 when the float16 copy is made, so a
+ * large value in a frame a row does not attend never reaches that row's
+ * output.  NaN values stay NaN and may spread to rows whose 64-key tiles
+ * hold them.
  * Supported: D in {64, 128}; P >= 1; Nq % P == 0; Nk % P == 0.  The bf16
  * path reads and writes 16 bytes at a time: q, k, v, o and the workspace must
  * be 16-byte aligned (FSA_E_ARG otherwise).
@@ -341,7 +351,8 @@ fsa_status fsa_sparse_frame_attn(const void *q, const void *k, const void *v, in
  *                                transposed copy of v into `prepared`
  *                                (>= fsa_sparse_frame_attn_workspace_size
  *                                bytes, layout [B*H][ceil(Nk/8)][D][8]; keys
- *                                past Nk are zero).
+ *                                past Nk are zero; values beyond +-65504
+ *                                saturate, as above).
  *   fsa_sparse_frame_attn_prepared  the attention itself, reading that copy
  *                                instead of v.
  * fsa_sparse_frame_attn(v, workspace) equals prepare(v -> workspace)

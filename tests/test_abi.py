@@ -287,3 +287,4 @@ def test_split_attention_argument_checks(splits, ws_bytes, status, text):
                                                   BAD, 4, 0.0, splits, BAD, BAD, 1 << 40, BAD,
                                                   ws_bytes, None)
     assert st == status and text in fsa.last_error()
+
