@@ -72,6 +72,9 @@ _SIGS = {
                                               _psz]),
     "fsa_select_topk_frames": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "fsa_select_topk_frames_noalloc": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                                              _vp, _vp]),
     "fsa_select_hsa_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _i32, _psz]),
     "fsa_select_hsa_blocks": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -346,6 +349,28 @@ def select_topk_frames(q: torch.Tensor, k: torch.Tensor, P: int, h_begin: int, h
                                           _ptr(out), _ptr(scores), _ptr(ws), nbytes,
                                           _stream(dev)))
     return (out, scores) if return_scores else out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def select_topk_frames_noalloc(q: torch.Tensor, k: torch.Tensor, P: int, h_begin: int,
+                               h_end: int, q_group: int, cand_begin: int, cand_end: int,
+                               topk: int, out: torch.Tensor, scores: torch.Tensor | None = None):
+    """select_topk_frames through the allocation-free entry point: the caller
+    passes the output (int32 [B, H, G, topk], and optionally float64 scores
+    [B, H, G, cand_end - cand_begin]); the pooled sums use the library's
+    static device scratch (at most NOALLOC_SCRATCH_BYTES), and nothing is
+    allocated, here or in the library.  Returns out."""
+    dev = _on_gpu(q=q, k=k, out=out, scores=scores)
+    B, H, Nq, Nk, D = _qk_shapes(q, k)
+    G = Nq // (q_group * P) if q_group * P > 0 else 0
+    _expect(out, "out", torch.int32, (B, H, G, topk))
+    _expect(scores, "scores", torch.float64, (B, H, G, cand_end - cand_begin))
+    _check(_load().fsa_select_topk_frames_noalloc(
+        _ptr(q), _ptr(k), _dtype_code(q), B, H, Nq, Nk, D, P, h_begin, h_end, q_group,
+        cand_begin, cand_end, topk, _ptr(out), _ptr(scores), _stream(dev)))
+    return out
 
 
 def select_hsa_blocks(q: torch.Tensor, k: torch.Tensor, P: int, block: int, h_begin: int,

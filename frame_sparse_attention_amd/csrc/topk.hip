@@ -17,6 +17,8 @@
 //                 argmax beyond 1024 candidates), written in ascending order.
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "pooling.h"
 
 namespace {
@@ -149,15 +151,15 @@ extern "C" fsa_status fsa_select_topk_workspace_size(int32_t B, int32_t H, int32
   return FSA_OK;
 }
 
-extern "C" fsa_status fsa_select_topk_frames(const void *q, const void *k, int32_t dt, int32_t B,
-                                             int32_t H, int32_t Nq, int32_t Nk, int32_t D,
-                                             int32_t P, int32_t h_begin, int32_t h_end,
-                                             int32_t q_group, int32_t cand_begin,
-                                             int32_t cand_end, int32_t topk_k,
-                                             int32_t *out_frames, double *out_scores,
-                                             void *workspace, size_t workspace_bytes,
-                                             void *stream) {
-  fsa::clear_error();
+namespace {
+
+// Checks everything but the workspace; returns the workspace bytes the call
+// needs in *need (0 when there is nothing to compute).
+fsa_status check_select(int32_t dt, int32_t B, int32_t H, int32_t Nq, int32_t Nk, int32_t D,
+                        int32_t P, int32_t h_begin, int32_t h_end, int32_t q_group,
+                        int32_t cand_begin, int32_t cand_end, int32_t topk_k, const void *q,
+                        const void *k, const int32_t *out_frames, size_t *need) {
+  *need = 0;
   fsa_status st = check_args(B, H, Nq, D, P, q_group, cand_begin, cand_end);
   if (st != FSA_OK) return st;
   FSA_REQUIRE(dt == FSA_F32 || dt == FSA_BF16, FSA_E_DTYPE, "unknown dtype %d", dt);
@@ -174,18 +176,99 @@ extern "C" fsa_status fsa_select_topk_frames(const void *q, const void *k, int32
   const int Hs = h_end - h_begin;
   const int G = Nq / (q_group * P);
   if (B == 0 || Hs == 0 || G == 0) return FSA_OK;
-  FSA_REQUIRE(q && k && out_frames && workspace, FSA_E_ARG, "null pointer argument");
+  FSA_REQUIRE(q && k && out_frames, FSA_E_ARG, "null pointer argument");
+  *need = (size_t)B * Hs * ((size_t)G * q_group + F) * D * sizeof(double);
+  return FSA_OK;
+}
+
+// Pooling and selection with the pooled sums in `workspace` (>= the bytes
+// check_select reported; every byte the kernels read there they wrote first).
+fsa_status launch_select(int32_t dt, const void *q, const void *k, int32_t B, int32_t H,
+                         int32_t Nq, int32_t Nk, int32_t D, int32_t P, int32_t h_begin,
+                         int32_t h_end, int32_t q_group, int32_t cand_begin, int32_t cand_end,
+                         int32_t topk_k, int32_t *out_frames, double *out_scores,
+                         void *workspace, hipStream_t s) {
+  const int F = cand_end - cand_begin;
+  const int Hs = h_end - h_begin;
+  const int G = Nq / (q_group * P);
   const int Tq = G * q_group;
-  const size_t need = (size_t)B * Hs * (Tq + F) * D * sizeof(double);
-  FSA_REQUIRE(workspace_bytes >= need, FSA_E_CAPACITY, "workspace of %zu bytes < %zu needed",
-              workspace_bytes, need);
   double *qframe = static_cast<double *>(workspace);
   double *ksum = qframe + (size_t)B * Hs * Tq * D;
-  hipStream_t s = fsa::as_stream(stream);
   const long long blocks = (long long)B * Hs * (Tq + F);
   FSA_REQUIRE(blocks < (1LL << 31), FSA_E_SHAPE, "too many pooling segments (%lld)", blocks);
   launch_pool(dt, q, k, H, Nq, Nk, D, P, h_begin, Hs, Tq, cand_begin, F, blocks, qframe, ksum, s);
   hipLaunchKernelGGL(score_select_kernel, dim3(B * Hs * G), dim3(64), 0, s, qframe, ksum, H, D,
                      h_begin, Hs, G, q_group, cand_begin, F, topk_k, out_frames, out_scores);
   return fsa::check_launch("select_topk_frames");
+}
+
+// Scratch of the allocation-free entry point: one array per GPU, created with
+// the library's code object and held until the process ends.  Host code uses
+// the device address from hipGetSymbolAddress, resolved once per device with
+// that device current; the array's own name is only a host-side stand-in.
+static __device__ __align__(256) unsigned char scratch[FSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch[kMaxDevices];
+
+fsa_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  FSA_REQUIRE(e == hipSuccess, FSA_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  FSA_REQUIRE(dev >= 0 && dev < kMaxDevices, FSA_E_HIP, "device %d beyond the %d supported", dev,
+              kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    FSA_REQUIRE(e == hipSuccess && p != nullptr, FSA_E_HIP,
+                "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return FSA_OK;
+}
+
+}  // namespace
+
+extern "C" fsa_status fsa_select_topk_frames(const void *q, const void *k, int32_t dt, int32_t B,
+                                             int32_t H, int32_t Nq, int32_t Nk, int32_t D,
+                                             int32_t P, int32_t h_begin, int32_t h_end,
+                                             int32_t q_group, int32_t cand_begin,
+                                             int32_t cand_end, int32_t topk_k,
+                                             int32_t *out_frames, double *out_scores,
+                                             void *workspace, size_t workspace_bytes,
+                                             void *stream) {
+  fsa::clear_error();
+  size_t need = 0;
+  fsa_status st = check_select(dt, B, H, Nq, Nk, D, P, h_begin, h_end, q_group, cand_begin,
+                               cand_end, topk_k, q, k, out_frames, &need);
+  if (st != FSA_OK || need == 0) return st;
+  FSA_REQUIRE(workspace != nullptr, FSA_E_ARG, "null pointer argument");
+  FSA_REQUIRE(workspace_bytes >= need, FSA_E_CAPACITY, "workspace of %zu bytes < %zu needed",
+              workspace_bytes, need);
+  return launch_select(dt, q, k, B, H, Nq, Nk, D, P, h_begin, h_end, q_group, cand_begin,
+                       cand_end, topk_k, out_frames, out_scores, workspace,
+                       fsa::as_stream(stream));
+}
+
+extern "C" fsa_status fsa_select_topk_frames_noalloc(
+    const void *q, const void *k, int32_t dt, int32_t B, int32_t H, int32_t Nq, int32_t Nk,
+    int32_t D, int32_t P, int32_t h_begin, int32_t h_end, int32_t q_group, int32_t cand_begin,
+    int32_t cand_end, int32_t topk_k, int32_t *out_frames, double *out_scores, void *stream) {
+  fsa::clear_error();
+  size_t need = 0;
+  fsa_status st = check_select(dt, B, H, Nq, Nk, D, P, h_begin, h_end, q_group, cand_begin,
+                               cand_end, topk_k, q, k, out_frames, &need);
+  if (st != FSA_OK || need == 0) return st;
+  FSA_REQUIRE(need <= FSA_NOALLOC_SCRATCH_BYTES, FSA_E_CAPACITY,
+              "the pooled sums need %zu bytes, more than the %zu bytes of device scratch this "
+              "entry point has; use fsa_select_topk_frames with a workspace",
+              need, (size_t)FSA_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != FSA_OK) return st;
+  return launch_select(dt, q, k, B, H, Nq, Nk, D, P, h_begin, h_end, q_group, cand_begin,
+                       cand_end, topk_k, out_frames, out_scores, ws, fsa::as_stream(stream));
 }

@@ -20,7 +20,10 @@
  *    and ignored when it reads them.
  *  - The caller owns every buffer.  The library never allocates or frees
  *    device or host memory; scratch space comes in through explicit workspace
- *    arguments.  It keeps no state beyond the thread-local error text.
+ *    arguments.  It keeps no state beyond the thread-local error text, except
+ *    for the one allocation-free entry point below
+ *    (fsa_select_topk_frames_noalloc), whose scratch is a static device array
+ *    per GPU.
  *  - "device" functions only validate their host arguments, enqueue kernels
  *    on `stream` (a hipStream_t; NULL = the default stream) and return; the
  *    results are ready when the stream reaches that point.  Launch failures
@@ -202,6 +205,30 @@ fsa_status fsa_select_topk_frames(const void *q, const void *k, int32_t dt, int3
                                   int32_t cand_begin, int32_t cand_end, int32_t topk_k,
                                   int32_t *out_frames, double *out_scores, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* device.  fsa_select_topk_frames without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The pooled sums live in a
+ * static device array of FSA_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU it runs on until the process ends; the call itself
+ * allocates and frees nothing.  The array of the current device is used, so
+ * call it with the device of `stream` current.  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (concurrent streams, or
+ * threads) race and give undefined frames; calls ordered on one stream are
+ * safe.  The kernels write every scratch byte they read, so nothing needs to
+ * start at zero.  Arguments, results and errors as fsa_select_topk_frames,
+ * plus FSA_E_CAPACITY when the pooled sums, B * (h_end - h_begin) *
+ * (Nq/P + cand_end - cand_begin) * D * 8 bytes, exceed the array (checked
+ * before anything is launched), and FSA_E_HIP when the array's device
+ * address cannot be resolved. */
+#define FSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+fsa_status fsa_select_topk_frames_noalloc(const void *q, const void *k, int32_t dt, int32_t B,
+                                          int32_t H, int32_t Nq, int32_t Nk, int32_t D,
+                                          int32_t P, int32_t h_begin, int32_t h_end,
+                                          int32_t q_group, int32_t cand_begin,
+                                          int32_t cand_end, int32_t topk_k,
+                                          int32_t *out_frames, double *out_scores,
+                                          void *stream);
 
 /* ------------------------------------------------------------------------
  * Chunk-aware growth of the sparsity ratio  [LF §2.1: first chunk dense,

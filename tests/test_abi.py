@@ -24,7 +24,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(fsa.EXPORTED)
@@ -288,3 +288,15 @@ def test_split_attention_argument_checks(splits, ws_bytes, status, text):
                                                   ws_bytes, None)
     assert st == status and text in fsa.last_error()
 
+
+def test_noalloc_topk_refuses_inputs_beyond_its_scratch_without_a_gpu():
+    # 12 heads x (4096 + 57 pooled rows) x 128 x 8 B = 51 MB > 16 MiB: FSA_E_CAPACITY
+    # before the scratch address is looked up or anything is launched
+    st = lib.fsa_select_topk_frames_noalloc(BAD, BAD, 1, 1, 12, 4096 * 16, 60 * 16, 128, 16,
+                                            0, 12, 1, 0, 57, 8, BAD, None, None)
+    assert st == 4 and "scratch" in fsa.last_error()
+    assert fsa.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # argument errors come first, as in the workspace entry point
+    st = lib.fsa_select_topk_frames_noalloc(BAD, BAD, 1, 1, 12, 4680, 93600, 128, 1560, 0, 12,
+                                            3, 0, 57, 0, BAD, None, None)
+    assert st == 1 and "topk" in fsa.last_error()
