@@ -192,6 +192,64 @@ def time_ms(fn, reps: int = 20) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def rollout_row(dev):
+    """A 20-chunk autoregressive rollout into a growing 60-frame cache: the
+    chunk-aware growth schedule (host) sets each chunk's frame budget k_i, then
+    per chunk the memory heads' top-k_i frames are selected on the device, every
+    head's frame set is built there, and the attention runs on the cache (its
+    values converted once, before the rollout).  Timed: the schedule and all
+    20 chunks."""
+    import torch
+
+    import frame_sparse_attention_amd as fsa
+    import workloads as wl
+    w = wl.ar_rollout()
+    r = w.rollout
+    n, c, P = r["n_chunks"], w.chunk, w.P
+    q, k, v = (t.to(dev) for t in wl.make_qkv(w))
+    prep = fsa.prepare_values(v)
+    shapes = [wl.rollout_chunk(w, i) for i in range(n)]
+    cost = [float(s["dense_frame_pairs"]) for s in shapes]
+    cand = [max(1, s["candidates"]) for s in shapes]
+    mem = [h for h, p in enumerate(w.policies) if p["kind"] == wl.MEMORY]
+    qs = [q[:, :, s["offset"] * P:(s["offset"] + c) * P].contiguous() for s in shapes]
+    outs = [(torch.empty((w.B, w.H, c * P, w.D), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.H, c * P), dtype=torch.float32, device=dev)) for _ in shapes]
+
+    def rollout(counts=None):
+        _, bud, _ = fsa.cag_schedule(cost, r["s_target"], r["s_base"], r["s_max"], cand)
+        for i, s in enumerate(shapes):
+            pols = wl.rollout_policies(w, i, int(bud[i]))
+            sel = None
+            if i > 0:
+                sel = fsa.select_topk_frames(qs[i], k, P, mem[0], mem[-1] + 1, c, 0,
+                                             s["candidates"], int(bud[i]))
+            idx, cnt = fsa.build_frame_sets(pols, w.B, c, s["cached"], s["offset"], c, sel,
+                                            device=dev)
+            fsa.sparse_frame_attn_prepared(qs[i], k, prep, idx, cnt, P, out=outs[i][0],
+                                           out_lse=outs[i][1])
+            if counts is not None:
+                counts.append(int(cnt.to(torch.int64).sum()) * P * P)
+        return bud
+
+    counts = []
+    bud = rollout(counts)          # untimed: also counts the attended pairs
+    total_pairs = sum(counts)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 5
+    for _ in range(reps):
+        rollout()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    dense_pairs = sum(cost) * P * P * w.H
+    return {"workload": w.name, "chunks": n, "budgets_k_i": [int(b) for b in bud],
+            "ms_rollout": round(ms, 3), "attended_pairs": total_pairs,
+            "dense_pairs": int(dense_pairs),
+            "kept_fraction_of_dense": round(total_pairs / dense_pairs, 4),
+            "effective_TFLOP_per_s": round(4 * w.D * total_pairs / (ms * 1e-3) / 1e12, 1)}
+
+
 def aux_rows(dev):
     """The other hot-path rows at their workload shapes: frame pooling + top-k
     (AR chunk, memory heads 8-11) and the LSE merge against the HBM roof; the AR
@@ -269,6 +327,7 @@ def aux_rows(dev):
         "attended_pairs": hpairs,
         "effective_TFLOP_per_s": round(4 * hw.D * hpairs / (ms_hattn * 1e-3) / 1e12, 1)}
     del q, k, qd, kd, v, prep, idx, cnt, hidx, hcnt
+    out["cag_rollout"] = rollout_row(dev)
     # the long-video workload (H24, 126 frames x 3600 tokens, C33 W11 T_per8), one
     # step: inputs drawn on the device (same shape and distribution; the seeded
     # CPU recipe of the parity tests would take minutes at this size)

@@ -57,3 +57,20 @@ def test_frame_set_sizes_of_each_workload():
     w = wl.long_video(3)
     _, cnt = fs.build(w.policies[:1], w.B, w.Tq, w.Tk, w.offset, w.chunk)
     assert (cnt == 33).all()
+
+
+def test_rollout_chunks_grow_the_cache():
+    w = wl.ar_rollout()
+    shapes = [wl.rollout_chunk(w, i) for i in range(w.rollout["n_chunks"])]
+    assert [s["cached"] for s in shapes] == list(range(3, 61, 3))
+    assert shapes[-1]["candidates"] == 57 and shapes[0]["candidates"] == 0
+    assert [s["dense_frame_pairs"] for s in shapes[:3]] == [9, 18, 27]
+    # first chunk dense on every head; later memory heads keep k_i + 3 recent frames
+    for h, p in enumerate(wl.rollout_policies(w, 0, 1)):
+        _, cnt = fs.build([p], 1, 3, 3, 0, 3)
+        assert (cnt == 3).all(), h
+    pols = wl.rollout_policies(w, 7, 5)
+    assert [p["topk"] for p in pols[8:]] == [5] * 4
+    sel = [[[[0, 2, 4, 6, 8]]]]
+    _, cnt = fs.build(pols[8:9], 1, 3, 24, 21, 3, sel)
+    assert (cnt == 8).all()

@@ -63,6 +63,10 @@ class Workload:
     # leading channels (0 = none) and the frequency base
     rope_dims: int = 0
     rope_base: float = 10000.0
+    # autoregressive rollout driven by the chunk-aware growth schedule: number
+    # of chunks, schedule parameters (target sparsity, s_base, s_max) and the
+    # memory heads' recent frames; empty = no rollout
+    rollout: dict = field(default_factory=dict)
 
     @property
     def Nq(self) -> int:
@@ -130,6 +134,46 @@ def ar_chunk_rope() -> Workload:
     return dataclasses.replace(w, name="ar_chunk_rope_3x1560_cache60_rot42", rope_dims=42)
 
 
+def ar_rollout() -> Workload:
+    """Autoregressive rollout of 20 chunks of 3 frames x 1560 tokens, H=12, D=128,
+    into a KV cache that grows by one chunk per step up to the 60 frames of the
+    AR chunk workload.  Chunk i's queries are frames 3i..3i+2; it attends frames
+    0..3i+2 through the AR chunk's per-head sets: heads 0-3 local (last 6
+    frames), 4-7 anchor (frames 0-2 + last 6), 8-11 memory (the k_i best of the
+    history frames 0..3i-1 by pooled Q.K, plus the last 3).  k_i comes from the
+    chunk-aware growth schedule (target sparsity 0.6, s_base 0.9, s_max 0.95)
+    over the chunks' dense costs; chunk 0 is attended densely."""
+    w = ar_chunk()
+    return dataclasses.replace(
+        w, name="ar_rollout_20x3x1560_cache60", seed=6, Tq=60, Tk=60, offset=0,
+        rollout=dict(n_chunks=20, s_target=0.6, s_base=0.9, s_max=0.95, n_recent=3))
+
+
+def rollout_chunk(w: Workload, i: int) -> dict:
+    """Shape of chunk i of a rollout workload: its first query frame (= the KV
+    frame offset of its queries), the frames cached when it runs, its dense
+    cost in attended frame pairs (query frames x cached frames), and the
+    history frames a memory head chooses from (those before the recent ones)."""
+    c = w.chunk
+    offset = i * c
+    cached = offset + c
+    return dict(offset=offset, cached=cached, dense_frame_pairs=c * cached,
+                candidates=cached - w.rollout["n_recent"])
+
+
+def rollout_policies(w: Workload, i: int, k_i: int) -> list:
+    """Per-head policies of chunk i with the memory heads keeping k_i selected
+    frames; the first chunk, with no history yet, is dense (FULL) on the
+    memory heads, as the schedule attends the first chunk densely."""
+    out = []
+    for p in w.policies:
+        p = dict(p)
+        if p["kind"] == MEMORY:
+            p = policy(FULL) if i == 0 else dict(p, topk=k_i, n_recent=w.rollout["n_recent"])
+        out.append(p)
+    return out
+
+
 def block_policies(w: Workload) -> list:
     """The heads' policies in block units for a workload with `block` set: every
     frame count of a SINK_WINDOW / RANGE head is multiplied by the blocks per
@@ -174,7 +218,7 @@ def long_video(step: int = 0) -> Workload:
 
 
 ALL = {w().name: w for w in (tiny_f32, lvsa_shaped, ar_chunk, ar_chunk_hsa, ar_chunk_rope,
-                              decomposable, long_video)}
+                              ar_rollout, decomposable, long_video)}
 
 
 def _seed(cfg_seed: int, tensor: int, head: int) -> int:
