@@ -16,10 +16,9 @@ Readings (the page fixes neither the sizes nor the arithmetic):
     nb = P / Bs blocks per frame); query blocks and key blocks have the same
     size, and global block index = frame * nb + block-in-frame;
   * pooling is kept as float64 sums, as for the frame-level top-k: a block sum
-    adds its Bs tokens one at a time in ascending token order, and a frame sum
-    adds its nb block sums one at a time in ascending block order (the
-    coarse level is built from the fine one; in exact arithmetic it is the sum
-    over the frame's tokens);
+    is the exact sum of its Bs tokens and a frame sum the exact sum of its P
+    tokens, each rounded once to float64 (the coarse level is not built from
+    rounded fine sums, so no order of summation enters either);
   * scores are dot products of a query block sum with a frame sum (level 1) or
     a block sum (level 2), each product rounded, added in ascending channel
     order; ranking is (score descending, index ascending), as in topk.py;
@@ -42,43 +41,28 @@ from . import frame_sets, topk
 
 
 def block_sums(tokens: np.ndarray, Bs: int) -> np.ndarray:
-    """[N, D] tokens -> [N/Bs, D] float64 sums, each sequential over its tokens."""
-    x = np.asarray(tokens)
+    """[N, D] tokens -> [N/Bs, D]: each block's exact sum, rounded once to float64."""
+    x = np.asarray(tokens, dtype=np.float64)
     if x.shape[0] % Bs:
         raise ValueError("tokens do not split into whole blocks")
-    nblk = x.shape[0] // Bs
-    acc = np.zeros((nblk, x.shape[1]), dtype=np.float64)
-    rows = np.arange(nblk) * Bs
-    for p in range(Bs):
-        acc = acc + x[rows + p].astype(np.float64)
-    return acc
+    return np.stack([topk.exact_column_sums(x[i:i + Bs]) for i in range(0, x.shape[0], Bs)]) \
+        if x.shape[0] else np.zeros((0, x.shape[1]))
 
 
-def frame_sums_from_blocks(bsum: np.ndarray, nb: int) -> np.ndarray:
-    """[F*nb, D] block sums -> [F, D] frame sums, sequential over the blocks."""
-    b = np.asarray(bsum, dtype=np.float64)
-    if b.shape[0] % nb:
-        raise ValueError("blocks do not split into whole frames")
-    F = b.shape[0] // nb
-    acc = np.zeros((F, b.shape[1]), dtype=np.float64)
-    for i in range(nb):
-        acc = acc + b[np.arange(F) * nb + i]
-    return acc
-
-
-def select_blocks(qblock_sum: np.ndarray, kblocks: np.ndarray, nb: int, e: int, n_recent: int,
-                  kf: int, kb: int):
+def select_blocks(qblock_sum: np.ndarray, kblocks: np.ndarray, kframes: np.ndarray, nb: int,
+                  e: int, n_recent: int, kf: int, kb: int):
     """Block set of one query block.
 
-    qblock_sum [D]: the query block's sum.  kblocks [>= (e+1)*nb, D]: key block
-    sums of the head.  Returns (sorted block list, selected frames).
+    qblock_sum [D]: the query block's sum.  kblocks [>= (e+1)*nb, D] and
+    kframes [>= e+1, D]: key block sums and key frame sums of the head (frame
+    f's blocks are f*nb .. f*nb+nb-1).  Returns (sorted block list, selected
+    frames).
     """
     first_recent = e - n_recent + 1
     if n_recent < 0 or first_recent < 0:
         raise ValueError("recent frames reach before frame 0")
     cands = list(range(first_recent))
-    kframes = frame_sums_from_blocks(kblocks[: first_recent * nb], nb)
-    frames = topk.rank_topk(topk.frame_scores(qblock_sum, kframes), cands, kf)
+    frames = topk.rank_topk(topk.frame_scores(qblock_sum, kframes[:first_recent]), cands, kf)
     cand_blocks = [f * nb + i for f in frames for i in range(nb)]
     bscores = topk.frame_scores(qblock_sum, kblocks[cand_blocks])
     blocks = topk.rank_topk(bscores, cand_blocks, kb)
@@ -99,11 +83,12 @@ def hsa_lists(q_bh: np.ndarray, k_bh: np.ndarray, P: int, Bs: int, offset: int, 
     nb = P // Bs
     qb = block_sums(q_bh, Bs)
     kbs = block_sums(k_bh, Bs)
+    kfs = block_sums(k_bh, P)
     out = []
     for j in range(qb.shape[0]):
         tq = j * Bs // P
         e = frame_sets.chunk_last_frame(tq, chunk, offset)
-        blocks, _ = select_blocks(qb[j], kbs, nb, e, n_recent, kf, kb)
+        blocks, _ = select_blocks(qb[j], kbs, kfs, nb, e, n_recent, kf, kb)
         out.append(blocks)
     return out
 

@@ -56,6 +56,10 @@ def test_cag_rollout_matches_oracle_rollout():
     prep = fsa.prepare_values(v.to(DEV))       # the cache's values, converted once
     k64 = {h: k[0, h].double().numpy() for h in range(w.H)}
     v64 = {h: v[0, h].double().numpy() for h in range(w.H)}
+    # the oracle's pooled key frames, computed once: every chunk chooses among a
+    # prefix of the same history
+    ksum = {h: otopk.pooled_key_sums(k64[h], P, range(shapes[-1]["candidates"]))
+            for h in mem_heads}
     scale = 1.0 / np.sqrt(w.D)
     for i, s in enumerate(shapes):
         off, cached, k_i = s["offset"], s["cached"], int(bud[i])
@@ -75,9 +79,10 @@ def test_cag_rollout_matches_oracle_rollout():
         if i > 0:
             osel = [[[[]] for _ in range(w.H)]]
             for h in mem_heads:
-                f, _ = otopk.select_topk_frames(q[0, h].float().numpy(), k[0, h].float().numpy(),
-                                                P, np.arange(rows_q.start, rows_q.stop),
-                                                range(s["candidates"]), k_i)
+                f, _ = otopk.select_topk_frames(q[0, h].float().numpy(), k64[h], P,
+                                                np.arange(rows_q.start, rows_q.stop),
+                                                range(s["candidates"]), k_i,
+                                                ksum=ksum[h][:s["candidates"]])
                 osel[0][h] = [f]
         oidx, ocnt = ofs.build(pols, w.B, c, cached, off, c, osel, cap=idx.shape[3])
         np.testing.assert_array_equal(cnt.cpu().numpy(), ocnt)

@@ -16,17 +16,15 @@ import pytest
 from oracle import attention, frame_sets, hsa, topk
 
 
-def test_block_then_frame_summation_order():
-    # token order inside a 4-token frame: ((1e16 + 1) - 1e16) + 1 = 1;
-    # blocks of 2: (1e16 + 1) = 1e16 and (-1e16 + 1) = -1e16, frame = 0
+def test_block_and_frame_sums_are_exact_sums_of_tokens():
+    # blocks of 2: 1e16 + 1 and -1e16 + 1 are ties that round to even (+-1e16);
+    # the frame sum is the exact sum of its 4 tokens, 2 -- not the sum of the
+    # rounded block sums (0) nor any sequential order (1)
     x = np.array([[1e16], [1.0], [-1e16], [1.0]])
     assert hsa.block_sums(x, 2).tolist() == [[1e16], [-1e16]]
-    assert hsa.frame_sums_from_blocks(hsa.block_sums(x, 2), 2).tolist() == [[0.0]]
-    assert hsa.block_sums(x, 4).tolist() == [[1.0]]
+    assert hsa.block_sums(x, 4).tolist() == [[2.0]]
     with pytest.raises(ValueError):
         hsa.block_sums(x, 3)
-    with pytest.raises(ValueError):
-        hsa.frame_sums_from_blocks(np.zeros((5, 1)), 2)
 
 
 def _planted():
@@ -46,13 +44,14 @@ def _planted():
         for i, v in enumerate(vals):
             kblocks[f * 3 + i, 0] = v
             kblocks[f * 3 + i, 1] = 7 * f + i   # channel 1 is ignored by the query
-    return kblocks
+    kframes = kblocks.reshape(6, 3, 2).sum(axis=1)    # small integers: exact
+    return kblocks, kframes
 
 
 def test_planted_two_level_selection():
-    kblocks = _planted()
+    kblocks, kframes = _planted()
     q = np.array([1.0, 0.0])
-    blocks, frames = hsa.select_blocks(q, kblocks, nb=3, e=5, n_recent=1, kf=2, kb=4)
+    blocks, frames = hsa.select_blocks(q, kblocks, kframes, nb=3, e=5, n_recent=1, kf=2, kb=4)
     assert frames == [0, 3]                      # totals 16 and 9 beat 3, 2, 0
     # blocks of frames 0 and 3 by score: 11 (6), 9 (5), 10 (5), 0 (4), 1 (3), 2 (2)
     # -> 9, 10, 11 and 0, the tie 9/10 going to the lower index; then frame 5's blocks
@@ -62,9 +61,9 @@ def test_planted_two_level_selection():
 
 
 def test_planted_selection_with_more_recent_frames():
-    kblocks = _planted()
+    kblocks, kframes = _planted()
     q = np.array([1.0, 0.0])
-    blocks, frames = hsa.select_blocks(q, kblocks, nb=3, e=5, n_recent=3, kf=1, kb=2)
+    blocks, frames = hsa.select_blocks(q, kblocks, kframes, nb=3, e=5, n_recent=3, kf=1, kb=2)
     # candidates 0..2; frame 0 (9) wins; its blocks 0 (4), 1 (3)
     assert frames == [0]
     assert blocks == [0, 1] + list(range(9, 18))
@@ -84,7 +83,8 @@ def test_matches_exact_arithmetic(seed):
     e, n_recent, kf, kb = F - 1, 2, 3, 5
     qsum = hsa.block_sums(qtok, Bs)[0]
     kbl = hsa.block_sums(ktok, Bs)
-    blocks, frames = hsa.select_blocks(qsum, kbl, nb, e, n_recent, kf, kb)
+    kfr = hsa.block_sums(ktok, P)
+    blocks, frames = hsa.select_blocks(qsum, kbl, kfr, nb, e, n_recent, kf, kb)
     # exact sums over tokens (any order), exact scores
     qx = [sum(Fraction(float(qtok[p, d])) for p in range(Bs)) for d in range(D)]
     kx = [[sum(Fraction(float(ktok[b * Bs + p, d])) for p in range(Bs)) for d in range(D)]
@@ -109,8 +109,8 @@ def test_blocks_as_large_as_frames_reduce_to_memory_selection():
     q = rng.standard_normal((P, D))            # one query frame = one query block
     k = rng.standard_normal((F * P, D))
     e, n_recent, kf = F - 1, 3, 4
-    blocks, frames = hsa.select_blocks(hsa.block_sums(q, P)[0], hsa.block_sums(k, P), 1, e,
-                                       n_recent, kf, kf)
+    blocks, frames = hsa.select_blocks(hsa.block_sums(q, P)[0], hsa.block_sums(k, P),
+                                       hsa.block_sums(k, P), 1, e, n_recent, kf, kf)
     ref, _ = topk.select_topk_frames(q, k, P, range(P), frame_sets.memory_candidates(n_recent, e),
                                      kf)
     assert frames == ref
@@ -152,14 +152,14 @@ def test_query_blocks_of_one_chunk_share_the_history_end():
 
 
 def test_budget_errors():
-    kblocks = _planted()
+    kblocks, kframes = _planted()
     q = np.array([1.0, 0.0])
     with pytest.raises(ValueError):
-        hsa.select_blocks(q, kblocks, nb=3, e=5, n_recent=1, kf=6, kb=1)   # 5 candidates
+        hsa.select_blocks(q, kblocks, kframes, nb=3, e=5, n_recent=1, kf=6, kb=1)  # 5 cands
     with pytest.raises(ValueError):
-        hsa.select_blocks(q, kblocks, nb=3, e=5, n_recent=1, kf=1, kb=4)   # 3 blocks
+        hsa.select_blocks(q, kblocks, kframes, nb=3, e=5, n_recent=1, kf=1, kb=4)  # 3 blocks
     with pytest.raises(ValueError):
-        hsa.select_blocks(q, kblocks, nb=3, e=1, n_recent=3, kf=1, kb=1)
+        hsa.select_blocks(q, kblocks, kframes, nb=3, e=1, n_recent=3, kf=1, kb=1)
 
 
 @pytest.mark.parametrize("n_sink,window", [(0, 6), (3, 6), (1, 2)])

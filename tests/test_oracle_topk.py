@@ -2,11 +2,15 @@
 Head Forcing methodology §2, memory heads).
 
 Checked against: planted frames with a known order (exact small integers),
-exact rational arithmetic (fractions.Fraction) on random inputs, the fixed
-summation order (a case where sequential and pairwise sums differ), the ban on
-fused multiply-add (a case where fusing changes the bits), ties, and scaling.
+exact rational arithmetic (fractions.Fraction, whose conversion to float is
+correctly rounded) for every pooled sum -- on random inputs and on cases where
+every fixed summation order differs from the exact sum (cancellation, a
+rounding tie, a tie broken by a term far below it, exponent spans beyond 53
+bits) --, invariance under any reordering of the tokens, the ban on fused
+multiply-add in the scores, ties, and scaling.
 """
 
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -52,22 +56,60 @@ def test_matches_exact_arithmetic_ranking(seed):
     assert frames == sorted(order[:kk])
     for f in range(F):
         assert abs(scores[f] - float(exact[f])) <= 1e-9 * max(1.0, abs(float(exact[f])))
+    # the pooled sums themselves are the correctly rounded exact sums
+    qs = topk.pooled_query_sum(q, P)
+    assert qs.tolist() == [_rn_exact(q[:, d]) for d in range(D)]
+    ks = topk.pooled_key_sums(k, P, range(F))
+    assert ks[3].tolist() == [_rn_exact(k[3 * P:4 * P, d]) for d in range(D)]
 
 
-def test_query_pooling_is_frames_first_then_sequential():
-    # 1e16 + 1 rounds back to 1e16 (spacing 2).  One frame of 4 tokens:
-    # ((1e16+1)-1e16)+1 = 1.  Two frames of 2 tokens: frame sums 1e16 and -1e16,
-    # total 0 (a token-sequential order would give 1; the exact sum is 2).
+def _rn_exact(col) -> float:
+    """The exact sum of float64 values rounded to the nearest float64 (ties to
+    even): Fraction arithmetic is exact and int/int division in Python rounds
+    correctly."""
+    return float(sum(Fraction(float(x)) for x in col))
+
+
+def test_pooled_sums_are_the_exact_sum_rounded_once():
+    # 1e16 + 1 rounds back to 1e16 (spacing 2) in any sequential order: a
+    # token-sequential sum gives 1, frames-then-total gives 0, the exact sum is 2
     q = np.array([[1e16], [1.0], [-1e16], [1.0]])
-    assert topk.pooled_query_sum(q, 4).tolist() == [1.0]
-    assert topk.pooled_query_sum(q, 2).tolist() == [0.0]
+    assert topk.pooled_query_sum(q, 4).tolist() == [2.0]
+    assert topk.pooled_query_sum(q, 2).tolist() == [2.0]
+    assert topk.pooled_key_sums(np.vstack([q, [[5.0], [0.0], [0.0], [0.0]]]), 4,
+                                [0, 1]).tolist() == [[2.0], [5.0]]
     with pytest.raises(ValueError):
         topk.pooled_query_sum(q, 3)
 
 
-def test_key_pooling_is_sequential_in_p():
-    k = np.array([[1e16], [1.0], [-1e16], [1.0], [5.0], [0.0], [0.0], [0.0]])
-    assert topk.pooled_key_sums(k, 4, [0, 1]).tolist() == [[1.0], [5.0]]
+@pytest.mark.parametrize("col,expect", [
+    ([1.0, 2.0**-53], 1.0),                               # an exact tie: to even
+    ([1.0 + 2.0**-52, 2.0**-53], 1.0 + 2.0**-51),          # a tie: to even, upwards
+    ([1.0, 2.0**-53, 2.0**-105], 1.0 + 2.0**-52),          # just above the tie
+    ([2.0**-105, 2.0**-53, 1.0], 1.0 + 2.0**-52),          # the same, any order
+    ([3e38, 1e-38, -3e38], 1e-38),                         # bf16/fp32 extremes cancel
+    ([2.0**-149, 2.0**127, -(2.0**127)], 2.0**-149),       # fp32 subnormal survives
+    ([-0.0, -0.0], 0.0),                                   # zero is +0
+    ([0.1] * 10, 1.0),                                     # exact 10 * fl(0.1) rounds to 1
+])
+def test_pooled_sum_special_cases(col, expect):
+    got = topk.exact_column_sums(np.array(col)[:, None])[0]
+    assert got == expect and math.copysign(1.0, got) == math.copysign(1.0, expect)
+    assert got == _rn_exact(col) + 0.0
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_pooled_sums_match_rational_arithmetic_in_any_order(seed):
+    rng = np.random.default_rng(50 + seed)
+    N, D = 64, 6
+    # bf16-like values: 8 significant bits, exponents spread over 60 binades
+    mant = rng.integers(128, 256, size=(N, D)) * rng.choice([-1, 1], size=(N, D))
+    expo = rng.integers(-40, 20, size=(N, D))
+    x = np.ldexp(mant.astype(np.float64), expo - 7)
+    got = topk.exact_column_sums(x)
+    assert got.tolist() == [_rn_exact(x[:, d]) for d in range(D)]
+    perm = rng.permutation(N)
+    assert topk.exact_column_sums(x[perm]).tobytes() == got.tobytes()
 
 
 def test_scores_round_each_product_before_adding():
