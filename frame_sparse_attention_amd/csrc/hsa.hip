@@ -9,16 +9,17 @@
 // output lists are in block units, so the attention kernels run on them with
 // "frames" of `block` tokens.
 //
-// Arithmetic (fixed, so the lists are bit-reproducible): float64 sums; a block
-// sum adds its tokens in ascending order, a frame sum adds its block sums in
-// ascending order; a score adds rounded products in ascending channel order;
+// Arithmetic (fixed, so the lists are bit-reproducible): a block sum and a
+// frame sum are each the exact sum of their tokens rounded once to float64
+// (pooling.h); a score adds rounded products in ascending channel order;
 // ranking is (score descending, index ascending).  Three launches:
-//   pool         block sums of every query block and of every key block of the
-//                candidate frames (the shared pooling kernel)
-//   frame_sums   frame sums from the block sums
-//   select       one wavefront per (b, h, query block): frame scores, the kf
-//                best by rank, block scores over the chosen frames, the kb best
-//                by rank, then the ascending list with the recent frames.
+//   pool       float64 partial sums of the pieces of every query block and
+//              every key block of the candidate frames
+//   finalize   exact query-block, key-block and key-frame sums (a frame's
+//              sum from the pieces of its blocks)
+//   select     one wavefront per (b, h, query block): frame scores, the kf
+//              best by rank, block scores over the chosen frames, the kb best
+//              by rank, then the ascending list with the recent frames.
 #pragma clang fp contract(off)
 
 #include "pooling.h"
@@ -26,89 +27,6 @@
 namespace {
 
 constexpr int kMaxHsaCand = 4096;  // candidate frames, and candidate blocks per query block
-
-__global__ void __launch_bounds__(kPoolThreads) hsa_frame_sums_kernel(
-    const double *__restrict__ kblk, int D, int nb, int Fc, long long n_frames,
-    double *__restrict__ kframe) {
-  // one block per (b, hs, frame); frame sum = ordered sum of its nb block sums
-  const long long fid = blockIdx.x;
-  if (fid >= n_frames) return;
-  const double *src = kblk + fid * nb * D;
-  for (int d = threadIdx.x; d < D; d += kPoolThreads) {
-    double a = 0.0;
-    for (int i = 0; i < nb; ++i) a = a + src[(long long)i * D + d];
-    kframe[fid * D + d] = a;
-  }
-  (void)Fc;
-}
-
-// A NaN score (from non-finite inputs) ranks as -inf, so (score, index) stays
-// a strict total order and exactly k candidates are kept.
-__device__ inline double nan_last(double s) { return s != s ? -INFINITY : s; }
-
-// (score, index) order: higher score first, then lower index.
-__device__ inline bool hsa_better(double s1, int i1, double s2, int i2) {
-  return s1 > s2 || (s1 == s2 && i1 < i2);
-}
-
-// Marks in s_taken the k best of s_score[0..n) in the (score descending,
-// index ascending) order, a strict total order: up to 1024 candidates, each
-// lane counts for its candidates how many others come first and keeps those
-// with fewer than k (one pass of n comparisons per candidate); beyond that, k
-// rounds of a wavefront argmax.  Both give the same set.  Needs k <= n and
-// s_taken[0..n) cleared.
-__device__ void take_best(const double *s_score, unsigned char *s_taken, int n, int k) {
-  const int lane = threadIdx.x;
-  if (n <= 1024) {
-    for (int i = lane; i < n; i += 64) {
-      const double si = s_score[i];
-      int ahead = 0;
-      for (int j = 0; j < n; ++j) ahead += hsa_better(s_score[j], j, si, i) ? 1 : 0;
-      s_taken[i] = ahead < k ? 1 : 0;
-    }
-    __syncthreads();
-    return;
-  }
-  for (int round = 0; round < k; ++round) {
-    double bs = 0.0;
-    int bi = -1;
-    for (int i = lane; i < n; i += 64) {
-      if (s_taken[i]) continue;
-      const double s = s_score[i];
-      if (bi < 0 || hsa_better(s, i, bs, bi)) {
-        bs = s;
-        bi = i;
-      }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double os = __shfl_xor(bs, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi >= 0 && (bi < 0 || hsa_better(os, oi, bs, bi))) {
-        bs = os;
-        bi = oi;
-      }
-    }
-    if (lane == 0) s_taken[bi] = 1;
-    __syncthreads();
-  }
-}
-
-// Writes the indices i < n with s_taken[i] set, ascending, through emit(pos, i);
-// returns how many there were.
-template <typename Emit>
-__device__ int compact_taken(const unsigned char *s_taken, int n, Emit emit) {
-  const int lane = threadIdx.x;
-  int count = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + lane;
-    const bool flag = i < n && s_taken[i];
-    const unsigned long long mask = __ballot(flag);
-    const int before = __popcll(mask & ((1ull << lane) - 1ull));
-    if (flag) emit(count + before, i);
-    count += __popcll(mask);
-  }
-  return count;
-}
 
 __global__ void __launch_bounds__(64) hsa_select_kernel(
     const double *__restrict__ qblk, const double *__restrict__ kblk,
@@ -133,15 +51,11 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
 
   // level 1: frames
   const double *kf_base = kframe + bh * Fc * D;
-  for (int f = lane; f < first_recent; f += 64) {
+  for (int f = lane; f < first_recent; f += 64)
     s_score[f] = nan_last(ordered_dot(qs, kf_base + (long long)f * D, D));
-    s_taken[f] = 0;
-  }
   __syncthreads();
   take_best(s_score, s_taken, first_recent, kf);
-  compact_taken(s_taken, first_recent, [&](int pos, int f) {
-    if (pos < kf) s_frames[pos] = f;
-  });
+  compact_taken(s_taken, first_recent, kf, [&](int pos, int f) { s_frames[pos] = f; });
   __syncthreads();
 
   // level 2: blocks of the chosen frames; candidate c is block
@@ -151,16 +65,14 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   for (int c = lane; c < nbc; c += 64) {
     const long long blk = (long long)s_frames[c / nb] * nb + c % nb;
     s_score[c] = nan_last(ordered_dot(qs, kb_base + blk * D, D));
-    s_taken[c] = 0;
   }
   __syncthreads();
   take_best(s_score, s_taken, nbc, kb);
 
   const long long row = ((long long)b * H + h_begin + hs) * Gq + j;
   int32_t *out = idx + row * cap;
-  compact_taken(s_taken, nbc, [&](int pos, int c) {
-    if (pos < kb) out[pos] = s_frames[c / nb] * nb + c % nb;
-  });
+  compact_taken(s_taken, nbc, kb,
+                [&](int pos, int c) { out[pos] = s_frames[c / nb] * nb + c % nb; });
   const int n_rec = n_recent * nb;
   for (int r = lane; r < n_rec; r += 64) out[kb + r] = first_recent * nb + r;
   for (int p = kb + n_rec + lane; p < cap; p += 64) out[p] = -1;
@@ -203,9 +115,35 @@ fsa_status check_hsa(int32_t B, int32_t H, int32_t Nq, int32_t Nk, int32_t D, in
   return FSA_OK;
 }
 
-size_t hsa_workspace(int32_t B, int32_t Hs, const HsaShape &sh, int32_t D) {
-  const size_t per_head = (size_t)sh.Gq + (size_t)sh.Fc * sh.nb + (size_t)sh.Fc;
-  return (size_t)B * Hs * per_head * D * sizeof(double);
+// Workspace layout for Hs selected heads: query-block, key-block and
+// key-frame sums, then the pieces of the query-block and key-block families.
+// With ws == nullptr only the size is computed.
+struct HsaLayout {
+  SegFamily qf, kf;
+  double *qblk, *kblk, *kframe;
+  size_t bytes;
+};
+HsaLayout hsa_layout(const void *q, const void *k, int B, int H, int Nq, int Nk, int D,
+                     int block, int h_begin, int Hs, const HsaShape &sh, void *ws) {
+  HsaLayout L{};
+  L.qf = make_family(q, Nq, 0, block, sh.Gq, H, h_begin, Hs);
+  L.kf = make_family(k, Nk, 0, block, sh.Fc * sh.nb, H, h_begin, Hs);
+  const size_t qb = align256((size_t)B * Hs * sh.Gq * D * sizeof(double));
+  const size_t kb = align256((size_t)B * Hs * sh.Fc * sh.nb * D * sizeof(double));
+  const size_t kfb = align256((size_t)B * Hs * sh.Fc * D * sizeof(double));
+  L.bytes = qb + kb + kfb + family_part_bytes(L.qf, B, D) + family_part_bytes(L.kf, B, D);
+  if (ws != nullptr) {
+    unsigned char *p = static_cast<unsigned char *>(ws);
+    L.qblk = reinterpret_cast<double *>(p);
+    p += qb;
+    L.kblk = reinterpret_cast<double *>(p);
+    p += kb;
+    L.kframe = reinterpret_cast<double *>(p);
+    p += kfb;
+    place_family(L.qf, B, D, &p);
+    place_family(L.kf, B, D, &p);
+  }
+  return L;
 }
 
 }  // namespace
@@ -221,7 +159,9 @@ extern "C" fsa_status fsa_select_hsa_workspace_size(int32_t B, int32_t H, int32_
   fsa_status st = check_hsa(B, H, Nq, Nk, D, P, block, q_kv_offset, chunk, h_begin, h_end,
                             n_recent, &sh);
   if (st != FSA_OK) return st;
-  *bytes = sh.Tq > 0 ? hsa_workspace(B, h_end - h_begin, sh, D) : 0;
+  *bytes = sh.Tq > 0 ? hsa_layout(nullptr, nullptr, B, H, Nq, Nk, D, block, h_begin,
+                                  h_end - h_begin, sh, nullptr).bytes
+                     : 0;
   return FSA_OK;
 }
 
@@ -251,25 +191,24 @@ extern "C" fsa_status fsa_select_hsa_blocks(
   FSA_REQUIRE(cap >= need_cap && cap >= 1 && cap <= FSA_MAX_CAP, FSA_E_CAPACITY,
               "cap=%d must hold %lld blocks and lie in [1, %d]", cap, need_cap, FSA_MAX_CAP);
   FSA_REQUIRE(q && k && idx && cnt && workspace, FSA_E_ARG, "null pointer argument");
-  const size_t need = hsa_workspace(B, Hs, sh, D);
-  FSA_REQUIRE(workspace_bytes >= need, FSA_E_CAPACITY, "workspace of %zu bytes < %zu needed",
-              workspace_bytes, need);
-  double *qblk = static_cast<double *>(workspace);
-  double *kblk = qblk + (size_t)B * Hs * sh.Gq * D;
-  double *kframe = kblk + (size_t)B * Hs * sh.Fc * sh.nb * D;
+  HsaLayout L = hsa_layout(q, k, B, H, Nq, Nk, D, block, h_begin, Hs, sh, nullptr);
+  FSA_REQUIRE(workspace_bytes >= L.bytes, FSA_E_CAPACITY, "workspace of %zu bytes < %zu needed",
+              workspace_bytes, L.bytes);
+  L = hsa_layout(q, k, B, H, Nq, Nk, D, block, h_begin, Hs, sh, workspace);
   hipStream_t s = fsa::as_stream(stream);
-  const int Fb = sh.Fc * sh.nb;  // key blocks pooled per head
-  const long long pool_blocks = (long long)B * Hs * (sh.Gq + Fb);
-  FSA_REQUIRE(pool_blocks < (1LL << 31), FSA_E_SHAPE, "too many pooling segments (%lld)",
-              pool_blocks);
-  launch_pool(dt, q, k, H, Nq, Nk, D, block, h_begin, Hs, sh.Gq, 0, Fb, pool_blocks, qblk, kblk,
-              s);
-  const long long n_frames = (long long)B * Hs * sh.Fc;
-  if (n_frames > 0)
-    hipLaunchKernelGGL(hsa_frame_sums_kernel, dim3((unsigned)n_frames), dim3(kPoolThreads), 0, s,
-                       kblk, D, sh.nb, sh.Fc, n_frames, kframe);
-  hipLaunchKernelGGL(hsa_select_kernel, dim3((unsigned)(B * Hs * sh.Gq)), dim3(64), 0, s, qblk,
-                     kblk, kframe, H, D, h_begin, Hs, sh.Gq, sh.nb, sh.Fc, q_kv_offset, chunk,
-                     n_recent, topk_frames, topk_blocks, cap, idx, cnt);
+  const long long pieces = (long long)(family_pieces(L.qf, B) + family_pieces(L.kf, B));
+  FSA_REQUIRE(pieces < (1LL << 31), FSA_E_SHAPE, "too many pooling pieces (%lld)", pieces);
+  // one-piece blocks are summed exactly by the pooling kernel itself; frames
+  // (nb blocks each, or blocks of several pieces) go through finalize
+  SegFamily qf = L.qf, kf = L.kf;
+  if (qf.pieces == 1) qf.direct = L.qblk;
+  if (kf.pieces == 1) kf.direct = L.kblk;
+  launch_pool(dt, pool_vec(dt, D, q, k), qf, kf, B, D, s);
+  launch_finalize(dt, qf.pieces == 1 ? no_final() : FinalFamily{L.qf, 1, L.qblk},
+                  kf.pieces == 1 ? no_final() : FinalFamily{L.kf, 1, L.kblk},
+                  FinalFamily{L.kf, sh.nb, L.kframe}, B, D, s);
+  hipLaunchKernelGGL(hsa_select_kernel, dim3((unsigned)(B * Hs * sh.Gq)), dim3(64), 0, s,
+                     L.qblk, L.kblk, L.kframe, H, D, h_begin, Hs, sh.Gq, sh.nb, sh.Fc,
+                     q_kv_offset, chunk, n_recent, topk_frames, topk_blocks, cap, idx, cnt);
   return fsa::check_launch("select_hsa_blocks");
 }

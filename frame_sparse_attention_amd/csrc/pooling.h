@@ -1,10 +1,33 @@
-// Float64 pooling of token segments (a query frame or block, a key frame or
-// block) shared by the frame-level top-k and the two-level block selection.
-// Every channel sum is one sequential chain in ascending token order, and
-// floating-point contraction is off, so the sums are reproducible bit for bit.
+// Float64 pooling of token segments (a query group or block, a key frame or
+// block) shared by the frame-level top-k and the two-level block selection
+// (Light Forcing §2.2: query and key tokens are compressed by mean pooling).
+//
+// A pooled sum is the exact sum of the segment's tokens in each channel,
+// rounded once to float64 (nearest, ties to even): it has no order of
+// summation, so the work can be cut any way.  Two launches:
+//
+//   pool_pieces_kernel  HBM-bound.  Each segment is cut into balanced pieces
+//       of at most 128 rows; one 256-thread block per piece streams its rows
+//       with 16-byte loads (8 per thread in flight), adds them in float64 and
+//       records the smallest and largest magnitude it saw.  Output per piece:
+//       D float64 partial sums and two magnitude keys.
+//   finalize_kernel  one wavefront per segment.  When the segment's magnitudes
+//       span few enough binades (fsa_exact::exact_by_range), every float64
+//       partial sum above was exact, in any order, so the pieces' sums add up
+//       to the exact sum.  Otherwise the segment's rows are read again and
+//       summed exactly (fsa_exact::ExactSum), then rounded once.  On bfloat16
+//       data the first case holds unless one segment mixes magnitudes about
+//       2^34 apart; float32 data takes the second case more often.
+//
+// A family of segments is a regular layout: for each selected head, `nseg`
+// segments of `seg_rows` rows starting at row `row0` of that head, each cut
+// into `pieces` pieces of `piece_rows` rows (the last one shorter).  Piece
+// results are stored segment-major, so the pieces of `group` consecutive
+// segments (e.g. the blocks of one frame) are consecutive as well.
 #pragma once
 #pragma clang fp contract(off)
 
+#include "exact_sum.h"
 #include "fsa_internal.h"
 
 namespace {
@@ -14,287 +37,389 @@ struct Bf16 {
   uint16_t bits;
 };
 
-// Pooling of one segment of rows (a query group, or one key frame) of one
-// head, for 128 channels per block: chunks of kRowsPerChunk rows are staged
-// through LDS with 16-byte loads (two chunks in flight), then thread d adds
-// its column one row at a time in ascending row order.  The float64 adds of a
-// channel form one sequential chain, exactly as the definition orders them;
-// the memory traffic around that chain is bulk and overlapped.
-constexpr int kPoolThreads = 128;
-constexpr int kRowsPerChunk = 32;
-constexpr int kMaxPoolD = 256;  // LDS: 2 chunks x 32 rows x 256 x 4 B = 64 KB at most
+constexpr int kPoolThreads = 256;
+constexpr int kPoolUnroll = 8;     // row steps issued together: loads in flight per thread
+constexpr int kPieceRows = 128;    // rows per piece at most (independent of dtype and alignment)
+constexpr int kMaxPoolD = 256;
 
-template <typename T>
-__device__ inline double elem_as_double(const T *row_tile, int r, int d, int D);
-template <>
-__device__ inline double elem_as_double<float>(const float *t, int r, int d, int D) {
-  return (double)t[r * D + d];
-}
-template <>
-__device__ inline double elem_as_double<Bf16>(const Bf16 *t, int r, int d, int D) {
-  return (double)__uint_as_float((uint32_t)t[r * D + d].bits << 16);
-}
+struct SegFamily {
+  const void *src;        // [B][H][head_rows][D] tensor
+  long long head_rows;    // rows of one head in src (Nq or Nk)
+  long long row0;         // first row of segment 0 inside a head
+  int seg_rows;           // rows per segment
+  int nseg;               // segments per selected head
+  int H;                  // heads per batch entry in src
+  int h_begin;            // first selected head
+  int nheads;             // selected heads (b-major: B * nheads segments lists)
+  int pieces;             // pieces per segment
+  int piece_rows;         // rows per piece (the last piece of a segment may be shorter)
+  double *part;           // [segments * pieces][D] float64 partial sums
+  uint32_t *keys;         // [segments * pieces][2] magnitude keys (min - 1, max)
+  double *direct;         // one-piece segments: [segments][D] exact sums written by the
+                          // pooling block itself (nullptr: left to finalize_kernel)
+  long long count() const { return (long long)nheads * nseg; }  // per batch entry
+};
 
-// Adds rows [0, rows) of the LDS chunk `t` into this thread's channel sums.
-template <typename T>
-__device__ inline void add_chunk(const T *t, int rows, int D, double *acc) {
-  const int tid = threadIdx.x;
-  for (int i = 0; i * kPoolThreads + tid < D; ++i) {
-    const int d = i * kPoolThreads + tid;
-    double a = acc[i];
-    if (rows == kRowsPerChunk) {
-      // read the whole column chunk first (independent LDS loads), then add in order
-      double x[kRowsPerChunk];
-#pragma unroll
-      for (int r = 0; r < kRowsPerChunk; ++r) x[r] = elem_as_double<T>(t, r, d, D);
-#pragma unroll
-      for (int r = 0; r < kRowsPerChunk; ++r) a = a + x[r];
-    } else {
-      for (int r = 0; r < rows; ++r) a = a + elem_as_double<T>(t, r, d, D);
-    }
-    acc[i] = a;
-  }
+// First row (in src) of segment `s` of family f for batch entry b, head slot hs.
+__device__ inline long long seg_first_row(const SegFamily &f, long long seg) {
+  const long long per_b = (long long)f.nheads * f.nseg;
+  const int b = (int)(seg / per_b);
+  const long long r = seg % per_b;
+  const int hs = (int)(r / f.nseg);
+  const int s = (int)(r % f.nseg);
+  const long long head = (long long)b * f.H + f.h_begin + hs;
+  return head * f.head_rows + f.row0 + (long long)s * f.seg_rows;
 }
 
-// s_waitcnt immediates: vmcnt(n) with expcnt and lgkmcnt at their maxima
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
+// 16-byte unit loads of VEC elements (VEC = 16 / sizeof(T)), or single
+// elements (VEC = 1) when rows are not 16-byte multiples or not aligned.
+template <typename T, int VEC>
+struct Unit {
+  uint32_t w[VEC * sizeof(T) / 4 > 0 ? VEC * sizeof(T) / 4 : 1];
+};
 
-// Sums rows [row0, row0 + nrows) of `src` (row stride D) into out[0..D).
-// Chunks of kRowsPerChunk rows stream from HBM into an LDS ring of kRing
-// slots with global_load_lds (no registers in flight), kRing - 1 chunks ahead
-// of the chunk being added; rows past the segment repeat its last row (in
-// bounds, never added).  Needs a chunk of whole 1 KB wavefront transfers.
-constexpr int kRing = 8;
-template <typename T>
-__device__ void pool_segment_dma(const T *__restrict__ src, long long row0, int nrows, int D,
-                                 unsigned char *lds, double *__restrict__ out) {
-  const int tid = threadIdx.x, lane = tid % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int row_bytes = D * (int)sizeof(T);
-  const int chunk_bytes = kRowsPerChunk * row_bytes;
-  const int per_wave = chunk_bytes / 1024 / (kPoolThreads / 64);  // DMA instructions per wave
-  const int nchunks = (nrows + kRowsPerChunk - 1) / kRowsPerChunk;
-  const char *base = reinterpret_cast<const char *>(src) + row0 * row_bytes;
-  auto issue = [&](int c) {
-    unsigned char *slot = lds + (c % kRing) * chunk_bytes;
-    for (int i = 0; i < per_wave; ++i) {
-      const int unit = (i * (kPoolThreads / 64) + wave) * 64 + lane;  // 16-byte unit in chunk
-      int r = c * kRowsPerChunk + unit * 16 / row_bytes;
-      r = r < nrows ? r : nrows - 1;
-      const char *g = base + (long long)r * row_bytes + (unit * 16) % row_bytes;
-      __builtin_amdgcn_global_load_lds(
-          (const void *)g,
-          (__attribute__((address_space(3))) void *)(slot + (i * (kPoolThreads / 64) + wave) * 1024),
-          16, 0, 0);
-    }
-  };
-  double acc[kMaxPoolD / kPoolThreads];
-  for (int i = 0; i < kMaxPoolD / kPoolThreads; ++i) acc[i] = 0.0;
-  for (int c = 0; c < kRing - 1 && c < nchunks; ++c) issue(c);
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + kRing - 1 < nchunks) {
-      issue(c + kRing - 1);
-      // chunk c landed once at most kRing - 1 later chunks are outstanding
-      if (per_wave == 1) wait_vmcnt<kRing - 1>();
-      else if (per_wave == 2) wait_vmcnt<2 * (kRing - 1)>();
-      else if (per_wave == 4) wait_vmcnt<4 * (kRing - 1)>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();
-    const int rows = min(kRowsPerChunk, nrows - c * kRowsPerChunk);
-    add_chunk<T>(reinterpret_cast<const T *>(lds + (c % kRing) * chunk_bytes), rows, D, acc);
-    __syncthreads();  // slot c % kRing is refilled by the next issue
-  }
-  for (int i = 0; i * kPoolThreads + tid < D; ++i) out[i * kPoolThreads + tid] = acc[i];
-}
-
-// Fallback for shapes the DMA path cannot take: chunks go through registers.
-template <typename T>
-__device__ void pool_segment(const T *__restrict__ src, long long row0, int nrows, int D,
-                             T *tile /* LDS [kRowsPerChunk * D] */, double *__restrict__ out) {
-  const int tid = threadIdx.x;
-  const int nchunks = (nrows + kRowsPerChunk - 1) / kRowsPerChunk;
-  double acc[kMaxPoolD / kPoolThreads];
-  for (int i = 0; i < kMaxPoolD / kPoolThreads; ++i) acc[i] = 0.0;
-  for (int c = 0; c < nchunks; ++c) {
-    const int rows = min(kRowsPerChunk, nrows - c * kRowsPerChunk);
-    const T *g = src + (row0 + (long long)c * kRowsPerChunk) * D;
-    for (int u = tid; u < rows * D; u += kPoolThreads) tile[u] = g[u];
-    __syncthreads();
-    add_chunk<T>(tile, rows, D, acc);
-    __syncthreads();
-  }
-  for (int i = 0; i * kPoolThreads + tid < D; ++i) out[i * kPoolThreads + tid] = acc[i];
-}
-
-// One launch pools every query frame and every candidate key frame of the
-// selected heads (one block each).
-template <typename T>
-__global__ void __launch_bounds__(kPoolThreads) pool_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, int H, int Nq, int Nk, int D, int P,
-    int h_begin, int Hs, int Tq, int cand_begin, int F, bool use_dma,
-    double *__restrict__ qframe, double *__restrict__ ksum) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T *tile = reinterpret_cast<T *>(smem);
-  const long long bid = blockIdx.x;
-  const int chunk_bytes = kRowsPerChunk * D * (int)sizeof(T);
-  const int per_wave = chunk_bytes / 1024 / (kPoolThreads / 64);
-  const bool dma = use_dma && chunk_bytes % 2048 == 0 &&
-                   (per_wave == 1 || per_wave == 2 || per_wave == 4);
-  // block layout: b-major, then [Tq query frames | F key frames] per selected head
-  const int per_b = Hs * (Tq + F);
-  const int b = (int)(bid / per_b);
-  const int rem = (int)(bid % per_b);
-  if (rem < Hs * Tq) {
-    const int hs = rem / Tq, t = rem % Tq;
-    const long long head = (long long)b * H + h_begin + hs;
-    double *dst = qframe + ((long long)(b * Hs + hs) * Tq + t) * D;
-    if (dma)
-      pool_segment_dma<T>(q, head * Nq + (long long)t * P, P, D, smem, dst);
-    else
-      pool_segment<T>(q, head * Nq + (long long)t * P, P, D, tile, dst);
+template <typename T, int VEC>
+__device__ inline Unit<T, VEC> load_unit(const T *p) {
+  Unit<T, VEC> u;
+  if constexpr (VEC * sizeof(T) == 16) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    u.w[0] = v.x, u.w[1] = v.y, u.w[2] = v.z, u.w[3] = v.w;
+  } else if constexpr (sizeof(T) == 4) {
+    u.w[0] = __float_as_uint(*reinterpret_cast<const float *>(p));
   } else {
-    const int r2 = rem - Hs * Tq;
-    const int hs = r2 / F, fi = r2 % F;
-    const long long head = (long long)b * H + h_begin + hs;
-    double *dst = ksum + ((long long)(b * Hs + hs) * F + fi) * D;
-    if (dma)
-      pool_segment_dma<T>(k, head * Nk + (long long)(cand_begin + fi) * P, P, D, smem, dst);
-    else
-      pool_segment<T>(k, head * Nk + (long long)(cand_begin + fi) * P, P, D, tile, dst);
+    u.w[0] = (uint32_t)reinterpret_cast<const Bf16 *>(p)->bits;  // VEC = 1, bf16
+  }
+  return u;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Adds one unit into acc[0..VEC) and its magnitudes into the keys.  bf16 pairs
+// update 16-bit keys two at a time; float32 updates 32-bit keys.
+template <typename T, int VEC>
+__device__ inline void add_unit(const Unit<T, VEC> &u, double *acc, u16x2 &k16min,
+                                u16x2 &k16max, uint32_t &k32min, uint32_t &k32max) {
+  if constexpr (sizeof(T) == 2 && VEC > 1) {
+#pragma unroll
+    for (int e = 0; e < VEC / 2; ++e) {
+      const uint32_t w = u.w[e];
+      acc[2 * e] = acc[2 * e] + (double)__uint_as_float(w << 16);
+      acc[2 * e + 1] = acc[2 * e + 1] + (double)__uint_as_float(w & 0xFFFF0000u);
+      const u16x2 a = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+      const u16x2 one = {1, 1};
+      k16min = __builtin_elementwise_min(k16min, a - one);  // zeros wrap to 0xFFFF
+      k16max = __builtin_elementwise_max(k16max, a);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const uint32_t bits = sizeof(T) == 2 ? u.w[0] << 16 : u.w[e];
+      acc[e] = acc[e] + (double)__uint_as_float(bits);
+      const uint32_t a = bits & 0x7FFFFFFFu;
+      k32min = min(k32min, a - 1u);  // zero wraps to 0xFFFFFFFF
+      k32max = max(k32max, a);
+    }
   }
 }
 
-// One wavefront per segment, for rows of a power-of-two size between 16 and
-// 1024 bytes and D <= 128 even: lane t adds channels 2t and 2t+1 (two
-// independent float64 chains, each in ascending row order).  Rows stream
-// through an LDS ring of kWaveRing (2 or 4) chunks of 16 KB with global_load_lds,
-// kWaveRing - 1 chunks ahead; a single wavefront needs no barrier, since its
-// own vmcnt wait makes a chunk visible and the reads of a slot finish before
-// the adds that use them, i.e. before the slot is refilled.
-constexpr int kWaveChunk = 16384;  // bytes per ring slot: 16 DMA instructions of 1 KB
-
 template <typename T>
-__device__ inline void pair_as_double(const unsigned char *p, double &x0, double &x1);
+__device__ inline uint32_t elem_bits(const T *p);
 template <>
-__device__ inline void pair_as_double<float>(const unsigned char *p, double &x0, double &x1) {
-  const float2 v = *reinterpret_cast<const float2 *>(p);
-  x0 = (double)v.x;
-  x1 = (double)v.y;
+__device__ inline uint32_t elem_bits<float>(const float *p) {
+  return __float_as_uint(*p);
 }
 template <>
-__device__ inline void pair_as_double<Bf16>(const unsigned char *p, double &x0, double &x1) {
-  const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
-  x0 = (double)__uint_as_float(w << 16);
-  x1 = (double)__uint_as_float(w & 0xFFFF0000u);
+__device__ inline uint32_t elem_bits<Bf16>(const Bf16 *p) {
+  return (uint32_t)p->bits << 16;
 }
 
-template <typename T, int kWaveRing, int CSPLIT>
-__device__ void pool_segment_wave(const T *__restrict__ src, long long row0, int nrows, int D,
-                                  int cgroup, double *__restrict__ out) {
-  __shared__ __attribute__((aligned(16))) unsigned char ring[kWaveRing][kWaveChunk];
-  const int lane = threadIdx.x;
-  // this wavefront's channels: [cgroup * D / CSPLIT, (cgroup + 1) * D / CSPLIT)
-  const int Dw = D / CSPLIT;
-  const int row_stride = D * (int)sizeof(T);       // bytes between rows in memory
-  const int row_bytes = Dw * (int)sizeof(T);       // bytes of a row this wavefront stages
-  const int col0 = cgroup * row_bytes;
-  const int rows_per_chunk = kWaveChunk / row_bytes;
-  const int nchunks = (nrows + rows_per_chunk - 1) / rows_per_chunk;
-  const char *base = reinterpret_cast<const char *>(src) + row0 * row_stride;
-  auto issue = [&](int c) {
+// One block per piece of family a (pieces [0, na)) or b (the rest).
+template <typename T, int VEC>
+__global__ void __launch_bounds__(kPoolThreads) pool_pieces_kernel(SegFamily fa, SegFamily fb,
+                                                                   long long na, int D) {
+  // per-row-group partials; when the units of a row divide a wavefront, the
+  // row groups of one wavefront are first added with shuffles and only one
+  // partial per wavefront reaches LDS
+  __shared__ double s_red[kPoolThreads * VEC];
+  __shared__ uint32_t s_kmin, s_kmax;
+  long long pid = blockIdx.x;
+  const bool in_a = pid < na;
+  const SegFamily f = in_a ? fa : fb;
+  if (!in_a) pid -= na;
+  const long long seg = pid / f.pieces;
+  const int piece = (int)(pid % f.pieces);
+  const int first = piece * f.piece_rows;
+  const int nrows = min(f.piece_rows, f.seg_rows - first);
+  const T *src =
+      static_cast<const T *>(f.src) + (seg_first_row(f, seg) + first) * (long long)D;
+
+  const int U = D / VEC;                      // units per row
+  const int RS = kPoolThreads / U;            // rows per step
+  const int t = threadIdx.x;
+  const int u = t % U, rg = t / U;
+  if (t == 0) {
+    s_kmin = fsa_exact::kKeyMinInit;
+    s_kmax = fsa_exact::kKeyMaxInit;
+  }
+  double acc[VEC];
 #pragma unroll
-    for (int i = 0; i < kWaveChunk / 1024; ++i) {
-      const int unit = i * 64 + lane;  // 16-byte unit of the chunk
-      int r = c * rows_per_chunk + unit * 16 / row_bytes;
-      r = r < nrows ? r : nrows - 1;  // past the segment: repeat its last row (never added)
-      const char *g = base + (long long)r * row_stride + col0 + (unit * 16) % row_bytes;
-      __builtin_amdgcn_global_load_lds(
-          (const void *)g, (__attribute__((address_space(3))) void *)&ring[c % kWaveRing][i * 1024],
-          16, 0, 0);
-    }
-  };
-  // CSPLIT == 1: lane t adds channels 2t, 2t+1; CSPLIT == 2: lane t adds channel t
-  constexpr int kCh = CSPLIT == 1 ? 2 : 1;
-  const int ch = kCh * lane;
-  const bool active = ch < Dw;
-  double a0 = 0.0, a1 = 0.0;
-  for (int c = 0; c < kWaveRing - 1 && c < nchunks; ++c) issue(c);
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + kWaveRing - 1 < nchunks) {
-      issue(c + kWaveRing - 1);
-      wait_vmcnt<(kWaveChunk / 1024) * (kWaveRing - 1)>();  // chunk c has landed
-    } else {
-      wait_vmcnt<0>();
-    }
-    const int rows = min(rows_per_chunk, nrows - c * rows_per_chunk);
-    const unsigned char *t = ring[c % kWaveRing];
-    if (active) {
-      if (kCh == 2) {
-        for (int r = 0; r < rows; ++r) {
-          double x0, x1;
-          pair_as_double<T>(t + r * row_bytes + ch * (int)sizeof(T), x0, x1);
-          a0 = a0 + x0;
-          a1 = a1 + x1;
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+  u16x2 k16min = {0xFFFF, 0xFFFF}, k16max = {0, 0};
+  uint32_t k32min = fsa_exact::kKeyMinInit, k32max = fsa_exact::kKeyMaxInit;
+  if (rg < RS) {
+    for (int r0 = rg; r0 < nrows; r0 += kPoolUnroll * RS) {
+      Unit<T, VEC> x[kPoolUnroll];
+#pragma unroll
+      for (int i = 0; i < kPoolUnroll; ++i) {
+        const int r = r0 + i * RS;
+        if (r < nrows) {
+          x[i] = load_unit<T, VEC>(src + (long long)r * D + u * VEC);
+        } else {
+#pragma unroll
+          for (int j = 0; j < (int)(sizeof(x[i].w) / 4); ++j) x[i].w[j] = 0u;  // adds +0
         }
-      } else {
-        for (int r = 0; r < rows; ++r)
-          a0 = a0 + elem_as_double<T>(reinterpret_cast<const T *>(t + r * row_bytes), 0, ch, 0);
       }
+#pragma unroll
+      for (int i = 0; i < kPoolUnroll; ++i)
+        add_unit<T, VEC>(x[i], acc, k16min, k16max, k32min, k32max);
     }
   }
-  if (active) {
-    out[cgroup * Dw + ch] = a0;
-    if (kCh == 2) out[cgroup * Dw + ch + 1] = a1;
+  if constexpr (sizeof(T) == 2 && VEC > 1) {
+    const unsigned short m = min(k16min.x, k16min.y);
+    k32min = m == 0xFFFF ? fsa_exact::kKeyMinInit : ((((uint32_t)m + 1u) << 16) - 1u);
+    k32max = (uint32_t)max(k16max.x, k16max.y) << 16;
+  }
+  // block reduction: the partials of a channel are added in float64; every
+  // such sum is exact whenever the segment passes exact_by_range
+  for (int off = 32; off >= 1; off >>= 1) {
+    k32min = min(k32min, (uint32_t)__shfl_xor((int)k32min, off));
+    k32max = max(k32max, (uint32_t)__shfl_xor((int)k32max, off));
+  }
+  __syncthreads();
+  if (t % 64 == 0) {
+    atomicMin(&s_kmin, k32min);
+    atomicMax(&s_kmax, k32max);
+  }
+  const bool by_wave = U <= 64 && 64 % U == 0;   // U a power of two up to 64
+  int groups = RS;                                 // partials per channel in LDS
+  if (by_wave) {
+    // lanes l, l ^ U, l ^ 2U, ... of a wavefront hold the same unit
+    for (int off = U; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + __shfl_xor(acc[e], off);
+    }
+    groups = kPoolThreads / 64;
+    if ((t % 64) < U) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s_red[(t / 64) * D + u * VEC + e] = acc[e];
+    }
+  } else if (rg < RS) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s_red[rg * D + u * VEC + e] = acc[e];
+  }
+  __syncthreads();
+  double *out = f.part + pid * (long long)D;
+  // a segment of one piece is finished here: its exact sum, directly
+  const bool direct = f.direct != nullptr && f.pieces == 1;
+  const int mbits = sizeof(T) == 2 ? fsa_exact::kBf16Bits : fsa_exact::kF32Bits;
+  const bool cheap = fsa_exact::exact_by_range(s_kmin, s_kmax, f.seg_rows, mbits);
+  for (int d = t; d < D; d += kPoolThreads) {
+    double s = 0.0;
+    for (int g = 0; g < groups; ++g) s = s + s_red[g * D + d];
+    out[d] = s;
+    if (direct) {
+      if (!cheap) {
+        fsa_exact::ExactSum acc;
+        acc.clear();
+        for (int r = 0; r < nrows; ++r) acc.add(elem_bits<T>(src + (long long)r * D + d));
+        s = acc.rounded();
+      }
+      f.direct[seg * D + d] = s + 0.0;
+    }
+  }
+  if (t == 0) {
+    f.keys[2 * pid] = s_kmin;
+    f.keys[2 * pid + 1] = s_kmax;
   }
 }
 
-template <typename T, int kWaveRing, int CSPLIT>
-__global__ void __launch_bounds__(64) pool_wave_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, int H, int Nq, int Nk, int D, int P,
-    int h_begin, int Hs, int Tq, int cand_begin, int F, double *__restrict__ qframe,
-    double *__restrict__ ksum) {
-  const long long bid = blockIdx.x / CSPLIT;
-  const int cgroup = (int)(blockIdx.x % CSPLIT);
-  // layout: b-major, then [Tq query segments | F key segments] per selected head
-  const int per_b = Hs * (Tq + F);
-  const int b = (int)(bid / per_b);
-  const int rem = (int)(bid % per_b);
-  if (rem < Hs * Tq) {
-    const int hs = rem / Tq, t = rem % Tq;
-    const long long head = (long long)b * H + h_begin + hs;
-    pool_segment_wave<T, kWaveRing, CSPLIT>(q, head * Nq + (long long)t * P, P, D, cgroup,
-                         qframe + ((long long)(b * Hs + hs) * Tq + t) * D);
+// Final sums of a family of segments.  `group` consecutive segments of the
+// pooled family form one output segment (a frame made of its blocks); the
+// output segment has group * seg_rows rows.
+struct FinalFamily {
+  SegFamily pooled;   // the family whose pieces hold the partial sums
+  int group;          // pooled segments per output segment
+  double *out;        // [output segments][D]
+  long long count() const { return pooled.count() / group; }  // per batch entry
+};
+
+constexpr int kFinalThreads = 64;
+
+template <typename T>
+__global__ void __launch_bounds__(kFinalThreads) finalize_kernel(FinalFamily fa, FinalFamily fb,
+                                                                 FinalFamily fc, long long na,
+                                                                 long long nb, int D) {
+  long long sid = blockIdx.x;
+  const int which = sid < na ? 0 : (sid < na + nb ? 1 : 2);
+  sid -= which == 0 ? 0 : (which == 1 ? na : na + nb);
+  const FinalFamily ff = which == 0 ? fa : (which == 1 ? fb : fc);
+  const SegFamily &f = ff.pooled;
+  const int np = ff.group * f.pieces;             // pieces of this output segment
+  const long long p0 = sid * np;
+  const long long nrows = (long long)ff.group * f.seg_rows;
+  const int lane = threadIdx.x;
+  uint32_t kmin = fsa_exact::kKeyMinInit, kmax = fsa_exact::kKeyMaxInit;
+  for (int p = lane; p < np; p += kFinalThreads) {
+    kmin = min(kmin, f.keys[2 * (p0 + p)]);
+    kmax = max(kmax, f.keys[2 * (p0 + p) + 1]);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  const int mbits = sizeof(T) == 2 ? fsa_exact::kBf16Bits : fsa_exact::kF32Bits;
+  double *out = ff.out + sid * (long long)D;
+  if (fsa_exact::exact_by_range(kmin, kmax, nrows, mbits)) {
+    for (int d = lane; d < D; d += kFinalThreads) {
+      // every addition is exact here, so the partials are added as they come,
+      // eight loads in flight at a time
+      const double *pp = f.part + p0 * D + d;
+      double s = 0.0;
+      int p = 0;
+      for (; p + 8 <= np; p += 8) {
+        double x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = pp[(long long)(p + i) * D];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = s + x[i];
+      }
+      for (; p < np; ++p) s = s + pp[(long long)p * D];
+      out[d] = s + 0.0;
+    }
+    return;
+  }
+  // the first pooled segment of this output segment: its rows and the next
+  // group - 1 segments' rows are consecutive in memory
+  const T *src = static_cast<const T *>(f.src) + seg_first_row(f, sid * ff.group) * (long long)D;
+  for (int d = lane; d < D; d += kFinalThreads) {
+    fsa_exact::ExactSum acc;
+    acc.clear();
+    for (long long r = 0; r < nrows; ++r) acc.add(elem_bits<T>(src + r * D + d));
+    out[d] = acc.rounded();
+  }
+}
+
+// Pieces per segment and rows per piece (balanced) for `rows`-row segments.
+inline void piece_plan(int rows, int *pieces, int *piece_rows) {
+  *pieces = (rows + kPieceRows - 1) / kPieceRows;
+  *piece_rows = (rows + *pieces - 1) / *pieces;
+}
+
+// Unit width for rows of D elements of the given dtype: 16 bytes when rows
+// are 16-byte multiples and both tensors are 16-byte aligned, else 1 element.
+inline int pool_vec(int32_t dt, int D, const void *a, const void *b) {
+  const int esz = dt == FSA_BF16 ? 2 : 4;
+  const bool aligned =
+      ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15u) == 0;
+  return (aligned && (D * esz) % 16 == 0) ? 16 / esz : 1;
+}
+
+// Fills in the piece layout of a family for `rows`-row segments.
+inline SegFamily make_family(const void *src, long long head_rows, long long row0, int seg_rows,
+                             int nseg, int H, int h_begin, int nheads) {
+  SegFamily f{};
+  f.src = src;
+  f.head_rows = head_rows;
+  f.row0 = row0;
+  f.seg_rows = seg_rows;
+  f.nseg = nseg;
+  f.H = H;
+  f.h_begin = h_begin;
+  f.nheads = nheads;
+  piece_plan(seg_rows, &f.pieces, &f.piece_rows);
+  return f;
+}
+
+// A family with no segments (an unused launch slot).
+inline SegFamily no_family() {
+  SegFamily f{};
+  f.nseg = 1;
+  f.pieces = 1;
+  f.piece_rows = 1;
+  f.seg_rows = 1;
+  return f;
+}
+inline FinalFamily no_final() { return FinalFamily{no_family(), 1, nullptr}; }
+
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of the partial sums and keys of a family over B batch entries.
+inline size_t family_pieces(const SegFamily &f, int B) {
+  return (size_t)B * f.nheads * f.nseg * f.pieces;
+}
+inline size_t family_part_bytes(const SegFamily &f, int B, int D) {
+  const size_t n = family_pieces(f, B);
+  return align256(n * (size_t)D * sizeof(double)) + align256(n * 2 * sizeof(uint32_t));
+}
+// Carves the family's partials and keys out of `ws` (advanced past them).
+inline void place_family(SegFamily &f, int B, int D, unsigned char **ws) {
+  const size_t n = family_pieces(f, B);
+  f.part = reinterpret_cast<double *>(*ws);
+  *ws += align256(n * (size_t)D * sizeof(double));
+  f.keys = reinterpret_cast<uint32_t *>(*ws);
+  *ws += align256(n * 2 * sizeof(uint32_t));
+}
+
+// Pools families a and b (pieces), then finalizes up to three output families.
+template <typename T, int VEC>
+void launch_pool_t(const SegFamily &a, const SegFamily &b, int B, int D, hipStream_t s) {
+  const long long na = (long long)family_pieces(a, B), nbp = (long long)family_pieces(b, B);
+  if (na + nbp > 0)
+    hipLaunchKernelGGL((pool_pieces_kernel<T, VEC>), dim3((unsigned)(na + nbp)),
+                       dim3(kPoolThreads), 0, s, a, b, na, D);
+}
+
+inline void launch_pool(int32_t dt, int vec, const SegFamily &a, const SegFamily &b, int B, int D,
+                        hipStream_t s) {
+  if (dt == FSA_BF16) {
+    if (vec == 8)
+      launch_pool_t<Bf16, 8>(a, b, B, D, s);
+    else
+      launch_pool_t<Bf16, 1>(a, b, B, D, s);
   } else {
-    const int r2 = rem - Hs * Tq;
-    const int hs = r2 / F, fi = r2 % F;
-    const long long head = (long long)b * H + h_begin + hs;
-    pool_segment_wave<T, kWaveRing, CSPLIT>(k, head * Nk + (long long)(cand_begin + fi) * P, P, D,
-                                            cgroup,
-                         ksum + ((long long)(b * Hs + hs) * F + fi) * D);
+    if (vec == 4)
+      launch_pool_t<float, 4>(a, b, B, D, s);
+    else
+      launch_pool_t<float, 1>(a, b, B, D, s);
   }
 }
 
-// sum_d qs[d] * row[d] in ascending d, each product rounded before it is
-// added.  The row (global memory) is read 16 values at a time into registers
-// ahead of the ordered adds, so the loads overlap instead of each add waiting
-// for its own load.
+inline void launch_finalize(int32_t dt, const FinalFamily &a, const FinalFamily &b,
+                            const FinalFamily &c, int B, int D, hipStream_t s) {
+  const long long na = B * a.count(), nb = B * b.count(), nc = B * c.count();
+  if (na + nb + nc == 0) return;
+  const dim3 grid((unsigned)(na + nb + nc)), block(kFinalThreads);
+  if (dt == FSA_BF16)
+    hipLaunchKernelGGL(finalize_kernel<Bf16>, grid, block, 0, s, a, b, c, na, nb, D);
+  else
+    hipLaunchKernelGGL(finalize_kernel<float>, grid, block, 0, s, a, b, c, na, nb, D);
+}
+
+// sum_d qs[d] * row[d] in ascending d, each product rounded to float64 before
+// it is added (contraction is off in every file that includes this header).
+// The row (global memory) is read 64 values at a time into registers ahead of
+// the ordered adds, so the loads overlap instead of each add waiting for its
+// own load.
 __device__ inline double ordered_dot(const double *qs, const double *__restrict__ row, int D) {
   double acc = 0.0;
   int d0 = 0;
   if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) {
-    for (; d0 + 16 <= D; d0 += 16) {
-      double2 x[8];
+    for (; d0 + 64 <= D; d0 += 64) {
+      double2 x[32];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) x[t] = reinterpret_cast<const double2 *>(row + d0)[t];
+      for (int t = 0; t < 32; ++t) x[t] = reinterpret_cast<const double2 *>(row + d0)[t];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < 32; ++t) {
         const double p0 = qs[d0 + 2 * t] * x[t].x;
         acc = acc + p0;
         const double p1 = qs[d0 + 2 * t + 1] * x[t].y;
@@ -309,63 +434,70 @@ __device__ inline double ordered_dot(const double *qs, const double *__restrict_
   return acc;
 }
 
-// Pools every query segment [t*P, (t+1)*P) of Nq and every key segment
-// cand_begin + fi, fi < F, of the heads [h_begin, h_begin + Hs): one wavefront
-// per segment where the rows allow it, else pool_kernel.
-inline void launch_pool(int32_t dt, const void *q, const void *k, int H, int Nq, int Nk, int D,
-                        int P, int h_begin, int Hs, int Tq, int cand_begin, int F, long long blocks,
-                        double *qframe, double *ksum, hipStream_t s) {
-  const bool aligned =
-      ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) & 15u) == 0;
-  const int row_bytes = D * (dt == FSA_BF16 ? 2 : 4);
-  const bool pow2_row = row_bytes >= 16 && row_bytes <= 1024 && (row_bytes & (row_bytes - 1)) == 0;
-  if (aligned && pow2_row && D % 2 == 0 && D <= 128) {
-    // segments of at most two chunks fit a two-slot ring: smaller LDS, more
-    // wavefronts per CU; longer segments stream through four slots, and when
-    // a half row is still 128 bytes or more their channels are split over two
-    // wavefronts (one ordered chain per lane, half the instructions each)
-    const bool short_seg = P <= 2 * (kWaveChunk / row_bytes);
-    const bool split = !short_seg && row_bytes >= 256;
-    const dim3 grid((unsigned)(blocks * (split ? 2 : 1))), block(64);
-    if (dt == FSA_BF16) {
-      auto qq = static_cast<const Bf16 *>(q);
-      auto kk = static_cast<const Bf16 *>(k);
-      if (short_seg)
-        hipLaunchKernelGGL((pool_wave_kernel<Bf16, 2, 1>), grid, block, 0, s, qq, kk, H, Nq, Nk,
-                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
-      else if (split)
-        hipLaunchKernelGGL((pool_wave_kernel<Bf16, 4, 2>), grid, block, 0, s, qq, kk, H, Nq, Nk,
-                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
-      else
-        hipLaunchKernelGGL((pool_wave_kernel<Bf16, 4, 1>), grid, block, 0, s, qq, kk, H, Nq, Nk,
-                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
-    } else {
-      auto qq = static_cast<const float *>(q);
-      auto kk = static_cast<const float *>(k);
-      if (short_seg)
-        hipLaunchKernelGGL((pool_wave_kernel<float, 2, 1>), grid, block, 0, s, qq, kk, H, Nq, Nk,
-                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
-      else if (split)
-        hipLaunchKernelGGL((pool_wave_kernel<float, 4, 2>), grid, block, 0, s, qq, kk, H, Nq, Nk,
-                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
-      else
-        hipLaunchKernelGGL((pool_wave_kernel<float, 4, 1>), grid, block, 0, s, qq, kk, H, Nq, Nk,
-                           D, P, h_begin, Hs, Tq, cand_begin, F, qframe, ksum);
+// (score, index) order: higher score first, then lower index.  A NaN score
+// (from non-finite inputs) ranks as -inf, so the order stays a strict total
+// order and exactly k candidates are kept.
+__device__ inline double nan_last(double s) { return s != s ? -INFINITY : s; }
+__device__ inline bool score_before(double s1, int i1, double s2, int i2) {
+  return s1 > s2 || (s1 == s2 && i1 < i2);
+}
+
+// Marks in s_taken the k best of s_score[0..n) in (score desc, index asc)
+// order; one wavefront (64 threads), scores NaN-free, k <= n.  Up to 1024
+// candidates each lane counts, for its candidates, how many others come
+// first, and keeps those with fewer than k; beyond that, k rounds of a
+// wavefront argmax.  Both give the same set.
+__device__ inline void take_best(const double *s_score, unsigned char *s_taken, int n, int k) {
+  const int lane = threadIdx.x;
+  if (n <= 1024) {
+    for (int i = lane; i < n; i += 64) {
+      const double si = s_score[i];
+      int ahead = 0;
+      for (int j = 0; j < n; ++j) ahead += score_before(s_score[j], j, si, i) ? 1 : 0;
+      s_taken[i] = ahead < k ? 1 : 0;
     }
+    __syncthreads();
     return;
   }
-  if (dt == FSA_BF16) {
-    const size_t chunk = (size_t)kRowsPerChunk * D * sizeof(Bf16);
-    const size_t lds = aligned && chunk * kRing <= 65536 ? chunk * kRing : chunk;
-    hipLaunchKernelGGL(pool_kernel<Bf16>, dim3((unsigned)blocks), dim3(kPoolThreads), lds, s,
-                       static_cast<const Bf16 *>(q), static_cast<const Bf16 *>(k), H, Nq, Nk, D,
-                       P, h_begin, Hs, Tq, cand_begin, F, lds > chunk, qframe, ksum);
-  } else {
-    const size_t chunk = (size_t)kRowsPerChunk * D * sizeof(float);
-    const size_t lds = aligned && chunk * kRing <= 65536 ? chunk * kRing : chunk;
-    hipLaunchKernelGGL(pool_kernel<float>, dim3((unsigned)blocks), dim3(kPoolThreads), lds, s,
-                       static_cast<const float *>(q), static_cast<const float *>(k), H, Nq, Nk,
-                       D, P, h_begin, Hs, Tq, cand_begin, F, lds > chunk, qframe, ksum);
+  for (int i = lane; i < n; i += 64) s_taken[i] = 0;
+  __syncthreads();
+  for (int round = 0; round < k; ++round) {
+    double bs = 0.0;
+    int bi = -1;
+    for (int i = lane; i < n; i += 64) {
+      if (s_taken[i]) continue;
+      const double s = s_score[i];
+      if (bi < 0 || score_before(s, i, bs, bi)) {
+        bs = s;
+        bi = i;
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double os = __shfl_xor(bs, off);
+      const int oi = __shfl_xor(bi, off);
+      if (oi >= 0 && (bi < 0 || score_before(os, oi, bs, bi))) {
+        bs = os;
+        bi = oi;
+      }
+    }
+    if (lane == 0) s_taken[bi] = 1;
+    __syncthreads();
+  }
+}
+
+// Calls emit(pos, i) for the indices i < n with s_taken[i] set, pos counting
+// them in ascending i, for pos < limit; one wavefront.
+template <typename Emit>
+__device__ inline void compact_taken(const unsigned char *s_taken, int n, int limit, Emit emit) {
+  const int lane = threadIdx.x;
+  int count = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    const bool flag = i < n && s_taken[i];
+    const unsigned long long mask = __ballot(flag);
+    const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+    if (flag && pos < limit) emit(pos, i);
+    count += __popcll(mask);
   }
 }
 

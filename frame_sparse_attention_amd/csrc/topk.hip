@@ -4,17 +4,21 @@
 // history frames; Head Forcing methodology §2: memory heads).
 //
 // Pooling is kept as float64 sums (a mean differs by a positive factor, so
-// the ranking is unchanged and no division enters the bits).  Every sum runs
-// in one fixed sequential order and products are rounded before they are
-// added (fp contraction is off in this file), so the selected frames are
-// bit-reproducible.  Queries, like keys, are pooled per frame first; the
-// pooled query of a group is the ordered sum of its frame sums.  Two launches:
-//   pool          one block per (b, h, query frame) and per (b, h, key frame):
-//                 rows staged through LDS, one sequential float64 chain per
-//                 channel; every token is read once
-//   score_select  one wavefront per (b, h, group): scores, then the k best on
-//                 (score desc, frame asc) by rank (k rounds of a wavefront
-//                 argmax beyond 1024 candidates), written in ascending order.
+// the ranking is unchanged and no division enters the bits).  Each pooled sum
+// -- a query group's, a key frame's -- is the exact sum of its tokens rounded
+// once to float64, so it has no summation order (pooling.h).  The score of a
+// frame is the ascending-d dot product of the two sums with every product
+// rounded before it is added (fp contraction is off in this file), so the
+// selected frames are bit-reproducible.  Three launches:
+//   pool          one block per piece (<= 128 rows) of every query group and
+//                 every candidate key frame: float64 partial sums; every token
+//                 is read once
+//   finalize      one block per group / frame: the exact sums
+//   score_select  one wavefront per (b, h, group): scores (one lane per frame,
+//                 its row read 64 values ahead of the ordered adds), then the
+//                 k best on (score desc, frame asc) by rank (k rounds of a
+//                 wavefront argmax beyond 1024 candidates), written in
+//                 ascending order.
 #pragma clang fp contract(off)
 
 #include <mutex>
@@ -26,14 +30,9 @@ namespace {
 constexpr int kMaxCand = 4096;
 constexpr int kMaxTopk = 64;
 
-// (score, frame) order: higher score first, then lower frame.
-__device__ inline bool better(double s1, int f1, double s2, int f2) {
-  return s1 > s2 || (s1 == s2 && f1 < f2);
-}
-
 __global__ void __launch_bounds__(64) score_select_kernel(
-    const double *__restrict__ qframe, const double *__restrict__ ksum, int H, int D,
-    int h_begin, int Hs, int G, int q_group, int cand_begin, int F, int topk,
+    const double *__restrict__ qsum, const double *__restrict__ ksum, int H, int D,
+    int h_begin, int Hs, int G, int cand_begin, int F, int topk,
     int32_t *__restrict__ out_frames, double *__restrict__ out_scores) {
   __shared__ double s_score[kMaxCand];
   __shared__ unsigned char s_taken[kMaxCand];
@@ -42,79 +41,20 @@ __global__ void __launch_bounds__(64) score_select_kernel(
   const int g = blockIdx.x % G;
   const int hs = (blockIdx.x / G) % Hs;
   const int b = blockIdx.x / (G * Hs);
-  // pooled query of the group: its frame sums added one at a time in frame order
-  const double *qf = qframe + ((long long)(b * Hs + hs) * G * q_group + (long long)g * q_group) * D;
-  for (int d = lane; d < D; d += 64) {
-    double a = 0.0;
-    for (int f = 0; f < q_group; ++f) a = a + qf[(long long)f * D + d];
-    qs[d] = a;
-  }
+  const double *qg = qsum + ((long long)(b * Hs + hs) * G + g) * D;
+  for (int d = lane; d < D; d += 64) qs[d] = qg[d];
   __syncthreads();
   const double *ks = ksum + (long long)(b * Hs + hs) * F * D;
   const long long out_head = (long long)b * H + h_begin + hs;
   for (int fi = lane; fi < F; fi += 64) {
     const double acc = ordered_dot(qs, ks + (long long)fi * D, D);
-    // a NaN score (from non-finite inputs) ranks as -inf, so (score, frame)
-    // stays a strict total order and exactly topk frames are kept
-    s_score[fi] = acc != acc ? -INFINITY : acc;
-    s_taken[fi] = 0;
+    s_score[fi] = nan_last(acc);
     if (out_scores) out_scores[(out_head * G + g) * F + fi] = acc;
   }
   __syncthreads();
+  take_best(s_score, s_taken, F, topk);
   int32_t *out = out_frames + (out_head * G + g) * topk;
-  if (F <= 1024) {
-    // the topk best by rank: a candidate is kept when fewer than topk others
-    // come first in the strict (score desc, frame asc) order
-    for (int fi = lane; fi < F; fi += 64) {
-      const double si = s_score[fi];
-      int ahead = 0;
-      for (int j = 0; j < F; ++j) ahead += better(s_score[j], j, si, fi) ? 1 : 0;
-      s_taken[fi] = ahead < topk ? 1 : 0;
-    }
-    __syncthreads();
-    // ascending frames: position = kept candidates before this one
-    int count = 0;
-    for (int base = 0; base < F; base += 64) {
-      const int fi = base + lane;
-      const bool keep = fi < F && s_taken[fi];
-      const unsigned long long mask = __ballot(keep);
-      const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
-      if (keep && pos < topk) out[pos] = cand_begin + fi;
-      count += __popcll(mask);
-    }
-    return;
-  }
-  int mine = -1;  // frame selected in round == lane
-  for (int round = 0; round < topk; ++round) {
-    double bs = 0.0;
-    int bf = -1;
-    for (int fi = lane; fi < F; fi += 64) {
-      if (s_taken[fi]) continue;
-      const double s = s_score[fi];
-      if (bf < 0 || better(s, fi, bs, bf)) {
-        bs = s;
-        bf = fi;
-      }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double os = __shfl_xor(bs, off);
-      const int of = __shfl_xor(bf, off);
-      if (of >= 0 && (bf < 0 || better(os, of, bs, bf))) {
-        bs = os;
-        bf = of;
-      }
-    }
-    if (lane == round) mine = bf;
-    if (lane == 0) s_taken[bf] = 1;
-    __syncthreads();
-  }
-  // ascending order: the rank of each selected frame among the selected ones
-  int rank = 0;
-  for (int j = 0; j < topk; ++j) {
-    const int other = __shfl(mine, j);
-    if (other < mine) ++rank;
-  }
-  if (lane < topk) out[rank] = cand_begin + mine;
+  compact_taken(s_taken, F, topk, [&](int pos, int fi) { out[pos] = cand_begin + fi; });
 }
 
 fsa_status check_args(int32_t B, int32_t H, int32_t Nq, int32_t D, int32_t P, int32_t q_group,
@@ -132,9 +72,39 @@ fsa_status check_args(int32_t B, int32_t H, int32_t Nq, int32_t D, int32_t P, in
   return FSA_OK;
 }
 
-size_t workspace_bytes_for(int32_t B, int32_t H, int32_t Nq, int32_t D, int32_t P, int32_t F) {
-  const long long Tq = Nq / P;
-  return (size_t)B * H * (Tq + F) * D * sizeof(double);
+// Workspace layout for Hs selected heads: the pooled sums of the G query
+// groups and F candidate frames of each head, then the pieces' partial sums
+// and magnitude keys of both families.  With ws == nullptr only the size is
+// computed; otherwise the families' pointers are set.
+struct TopkLayout {
+  SegFamily qf, kf;
+  double *qsum, *ksum;
+  size_t bytes;
+};
+TopkLayout topk_layout(const void *q, const void *k, int B, int H, int Nq, int Nk, int D, int P,
+                       int h_begin, int Hs, int q_group, int cand_begin, int F, void *ws) {
+  TopkLayout L{};
+  const int G = Nq / (q_group * P);
+  L.qf = make_family(q, Nq, 0, q_group * P, G, H, h_begin, Hs);
+  L.kf = make_family(k, Nk, (long long)cand_begin * P, P, F, H, h_begin, Hs);
+  unsigned char *p = static_cast<unsigned char *>(ws);
+  const size_t qbytes = align256((size_t)B * Hs * G * D * sizeof(double));
+  const size_t kbytes = align256((size_t)B * Hs * F * D * sizeof(double));
+  L.bytes = qbytes + kbytes + family_part_bytes(L.qf, B, D) + family_part_bytes(L.kf, B, D);
+  if (ws != nullptr) {
+    L.qsum = reinterpret_cast<double *>(p);
+    p += qbytes;
+    L.ksum = reinterpret_cast<double *>(p);
+    p += kbytes;
+    place_family(L.qf, B, D, &p);
+    place_family(L.kf, B, D, &p);
+  }
+  return L;
+}
+
+size_t workspace_bytes_for(int32_t B, int32_t H, int32_t Nq, int32_t D, int32_t P,
+                           int32_t q_group, int32_t F) {
+  return topk_layout(nullptr, nullptr, B, H, Nq, 0, D, P, 0, H, q_group, 0, F, nullptr).bytes;
 }
 
 }  // namespace
@@ -147,7 +117,7 @@ extern "C" fsa_status fsa_select_topk_workspace_size(int32_t B, int32_t H, int32
   FSA_REQUIRE(bytes != nullptr, FSA_E_ARG, "bytes is NULL");
   fsa_status st = check_args(B, H, Nq, D, P, q_group, cand_begin, cand_end);
   if (st != FSA_OK) return st;
-  *bytes = workspace_bytes_for(B, H, Nq, D, P, cand_end - cand_begin);
+  *bytes = workspace_bytes_for(B, H, Nq, D, P, q_group, cand_end - cand_begin);
   return FSA_OK;
 }
 
@@ -177,7 +147,8 @@ fsa_status check_select(int32_t dt, int32_t B, int32_t H, int32_t Nq, int32_t Nk
   const int G = Nq / (q_group * P);
   if (B == 0 || Hs == 0 || G == 0) return FSA_OK;
   FSA_REQUIRE(q && k && out_frames, FSA_E_ARG, "null pointer argument");
-  *need = (size_t)B * Hs * ((size_t)G * q_group + F) * D * sizeof(double);
+  *need = topk_layout(q, k, B, H, Nq, Nk, D, P, h_begin, Hs, q_group, cand_begin, F, nullptr)
+              .bytes;
   return FSA_OK;
 }
 
@@ -191,14 +162,16 @@ fsa_status launch_select(int32_t dt, const void *q, const void *k, int32_t B, in
   const int F = cand_end - cand_begin;
   const int Hs = h_end - h_begin;
   const int G = Nq / (q_group * P);
-  const int Tq = G * q_group;
-  double *qframe = static_cast<double *>(workspace);
-  double *ksum = qframe + (size_t)B * Hs * Tq * D;
-  const long long blocks = (long long)B * Hs * (Tq + F);
-  FSA_REQUIRE(blocks < (1LL << 31), FSA_E_SHAPE, "too many pooling segments (%lld)", blocks);
-  launch_pool(dt, q, k, H, Nq, Nk, D, P, h_begin, Hs, Tq, cand_begin, F, blocks, qframe, ksum, s);
-  hipLaunchKernelGGL(score_select_kernel, dim3(B * Hs * G), dim3(64), 0, s, qframe, ksum, H, D,
-                     h_begin, Hs, G, q_group, cand_begin, F, topk_k, out_frames, out_scores);
+  TopkLayout L = topk_layout(q, k, B, H, Nq, Nk, D, P, h_begin, Hs, q_group, cand_begin, F,
+                             workspace);
+  const long long pieces = (long long)(family_pieces(L.qf, B) + family_pieces(L.kf, B));
+  FSA_REQUIRE(pieces < (1LL << 31), FSA_E_SHAPE, "too many pooling pieces (%lld)", pieces);
+  launch_pool(dt, pool_vec(dt, D, q, k), L.qf, L.kf, B, D, s);
+  launch_finalize(dt, FinalFamily{L.qf, 1, L.qsum}, FinalFamily{L.kf, 1, L.ksum}, no_final(), B,
+                  D, s);
+  hipLaunchKernelGGL(score_select_kernel, dim3(B * Hs * G), dim3(64), 0, s, L.qsum, L.ksum, H,
+                     D,
+                     h_begin, Hs, G, cand_begin, F, topk_k, out_frames, out_scores);
   return fsa::check_launch("select_topk_frames");
 }
 

@@ -101,7 +101,13 @@ def test_workspace_size_queries():
     assert lib.fsa_sparse_frame_attn_workspace_size(0, 1, 1, 13, 80, ctypes.byref(n)) == 3
     assert lib.fsa_select_topk_workspace_size(1, 12, 4680, 128, 1560, 3, 0, 57,
                                               ctypes.byref(n)) == 0
-    assert n.value == 1 * 12 * (3 + 57) * 128 * 8
+    # pooled sums of 12 query groups and 12 x 57 frames, then the pieces of at
+    # most 128 rows (37 per 4680-row group, 13 per 1560-row frame): 128 float64
+    # partial sums and 2 uint32 magnitude keys each; every array 256-byte aligned
+    a = lambda x: -(-x // 256) * 256
+    gp, fp = 12 * 37, 12 * 57 * 13
+    assert n.value == (a(12 * 128 * 8) + a(12 * 57 * 128 * 8) + a(gp * 128 * 8) + a(gp * 8)
+                       + a(fp * 128 * 8) + a(fp * 8))
 
 
 def _topk(**kw):
@@ -212,8 +218,13 @@ def test_select_hsa_workspace_size_and_empty_calls():
     n = ctypes.c_size_t(0)
     assert lib.fsa_select_hsa_workspace_size(1, 12, 4680, 93600, 128, 1560, 120, 57, 3, 8, 12,
                                              3, ctypes.byref(n)) == 0
-    # 4 heads x (39 query blocks + 57*13 key blocks + 57 frames) x 128 doubles
-    assert n.value == 4 * (39 + 57 * 13 + 57) * 128 * 8
+    # 4 heads x (39 query blocks + 57*13 key blocks + 57 frames) x 128 doubles of
+    # sums, then one piece per 120-token block (39 + 741 per head): 128 float64
+    # partial sums and 2 uint32 magnitude keys each; arrays 256-byte aligned
+    a = lambda x: -(-x // 256) * 256
+    qp, kp = 4 * 39, 4 * 57 * 13
+    assert n.value == (a(qp * 1024) + a(kp * 1024) + a(4 * 57 * 1024) + a(qp * 1024) + a(qp * 8)
+                       + a(kp * 1024) + a(kp * 8))
     # nothing to do: no heads, or no batch
     assert _hsa(h_begin=8, h_end=8) == 0
     assert _hsa(B=0) == 0
@@ -290,7 +301,7 @@ def test_split_attention_argument_checks(splits, ws_bytes, status, text):
 
 
 def test_noalloc_topk_refuses_inputs_beyond_its_scratch_without_a_gpu():
-    # 12 heads x (4096 + 57 pooled rows) x 128 x 8 B = 51 MB > 16 MiB: FSA_E_CAPACITY
+    # 12 heads x (4096 + 57) pooled sums of 128 float64 alone are 51 MB > 16 MiB: FSA_E_CAPACITY
     # before the scratch address is looked up or anything is launched
     st = lib.fsa_select_topk_frames_noalloc(BAD, BAD, 1, 1, 12, 4096 * 16, 60 * 16, 128, 16,
                                             0, 12, 1, 0, 57, 8, BAD, None, None)

@@ -201,12 +201,14 @@ def test_topk_many_candidates(n_cand, kk):
 
 
 @pytest.mark.parametrize("dtype,D,P", [
-    (torch.float32, 128, 300),   # long segments, channels split over two wavefronts
-    (torch.float32, 64, 500),    # float32 half rows of 128 bytes: split as well
-    (torch.bfloat16, 64, 700),   # 128-byte rows: one wavefront, four-slot ring
-    (torch.bfloat16, 128, 100),  # short segments: two-slot ring
-    (torch.bfloat16, 96, 90),    # 192-byte rows: the block-per-segment kernel
-    (torch.float32, 200, 40),    # 800-byte rows: the block-per-segment kernel
+    (torch.float32, 128, 300),   # 16-byte loads of 4 floats, 3 pieces per frame
+    (torch.float32, 64, 500),    # 16 rows per step, 4 pieces of 125 rows
+    (torch.bfloat16, 64, 700),   # 16-byte loads of 8 bf16, 32 rows per step
+    (torch.bfloat16, 128, 100),  # one piece per frame, 2 pieces per query group
+    (torch.bfloat16, 96, 90),    # 12 units per row: 21 rows per step, 4 threads idle
+    (torch.float32, 200, 40),    # 50 units per row, 5 rows per step
+    (torch.bfloat16, 60, 33),    # 120-byte rows: element-wise loads
+    (torch.float32, 30, 129),    # 120-byte rows: element-wise loads, 2 pieces per frame
 ])
 def test_topk_pooling_paths(dtype, D, P):
     g = torch.Generator().manual_seed(D * 1000 + P)
@@ -220,3 +222,54 @@ def test_topk_pooling_paths(dtype, D, P):
     of, os_ = _oracle_topk(q, k, P, 0, H, 2, 0, 12, 4)
     np.testing.assert_array_equal(frames.cpu().numpy(), of)
     assert np.array_equal(scores.cpu().numpy(), os_)
+
+
+def _wide_spread(shape, g, binades=200):
+    """bf16-exact values whose exponents spread over `binades` binades, with
+    exact opposites planted, so pooled segments fail the cheap exactness test
+    and are summed exactly on the device."""
+    m = torch.randint(128, 256, shape, generator=g).float()
+    e = torch.randint(-binades // 2, binades // 2, shape, generator=g).float()
+    s = torch.randint(0, 2, shape, generator=g).float() * 2 - 1
+    x = s * m * torch.exp2(e - 7)
+    x[..., 1::5, :] = -x[..., 0::5, :][..., : x[..., 1::5, :].shape[-2], :]
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_topk_exact_sums_of_wide_spread_values(dtype):
+    # every pooled sum is the exact sum rounded once: the device's exact path
+    # (segments spanning ~2^200) must give the oracle's bits
+    g = torch.Generator().manual_seed(31)
+    B, H, P, D = 1, 2, 40, 64
+    q = _wide_spread((B, H, 2 * P, D), g).to(dtype)
+    k = _wide_spread((B, H, 9 * P, D), g).to(dtype)
+    k[0, 0, 3 * P:4 * P] = q[0, 0, :P]          # a frame that matches the query well
+    _say(f"top-k over wide-spread values ({dtype})")
+    frames, scores = fsa.select_topk_frames(q.to(DEV), k.to(DEV), P, 0, H, 2, 0, 9, 3,
+                                            return_scores=True)
+    torch.cuda.synchronize()
+    of, os_ = _oracle_topk(q, k, P, 0, H, 2, 0, 9, 3)
+    np.testing.assert_array_equal(frames.cpu().numpy(), of)
+    assert np.array_equal(scores.cpu().numpy(), os_), "fp64 scores differ in some bit"
+
+
+def test_topk_pooling_is_exact_not_sequential():
+    # one key frame whose tokens are 2^100, 1, -2^100, 1 per channel: any
+    # sequential float64 order loses the ones; the exact sum is 2
+    P, D = 4, 64
+    q = torch.ones(1, 1, P, D)
+    k = torch.zeros(1, 1, 3 * P, D)
+    k[0, 0, 0] = 2.0**100
+    k[0, 0, 1] = 1.0
+    k[0, 0, 2] = -(2.0**100)
+    k[0, 0, 3] = 1.0                 # frame 0: exact sum 2 per channel
+    k[0, 0, P:2 * P] = 0.25          # frame 1: sum 1 per channel
+    k[0, 0, 2 * P:] = 0.125          # frame 2: sum 0.5 per channel
+    _say("top-k: cancellation inside one frame")
+    for dtype in (torch.float32, torch.bfloat16):
+        frames, scores = fsa.select_topk_frames(q.to(dtype).to(DEV), k.to(dtype).to(DEV), P, 0,
+                                                1, 1, 0, 3, 1, return_scores=True)
+        torch.cuda.synchronize()
+        assert frames.cpu().numpy().ravel().tolist() == [0]
+        assert scores.cpu().numpy().ravel().tolist() == [4.0 * 2 * D, 4.0 * D, 4.0 * 0.5 * D]

@@ -153,3 +153,28 @@ def test_hsa_attention_small_all_rows(dt):
     rows = np.arange(w.Nq)
     o_ref, l_ref = oracle_rows(q, k, v, idx, cnt, w.block, rows)
     assert_close(o.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, dt, f"hsa small {dt} all rows")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_select_hsa_blocks_exact_sums_of_wide_spread_values(dtype):
+    # block and frame sums are exact sums of tokens rounded once; values spread
+    # over ~2^200 with planted opposites make the device sum them exactly
+    B, H, D, Tq, Tk, P, block = 1, 2, 64, 2, 9, 12, 4
+    offset, chunk, n_recent, kf, kb = 7, 2, 2, 3, 5
+    g = torch.Generator().manual_seed(32)
+
+    def spread(n):
+        m = torch.randint(128, 256, (B, H, n, D), generator=g).float()
+        e = torch.randint(-100, 100, (B, H, n, D), generator=g).float()
+        s = torch.randint(0, 2, (B, H, n, D), generator=g).float() * 2 - 1
+        x = s * m * torch.exp2(e - 7)
+        x[:, :, 1::3] = -x[:, :, 0::3][:, :, : x[:, :, 1::3].shape[2]]
+        return x.to(dtype)
+
+    q, k = spread(Tq * P), spread(Tk * P)
+    _say(f"select_hsa_blocks over wide-spread values ({dtype})")
+    idx, cnt = fsa.select_hsa_blocks(q.to(DEV), k.to(DEV), P, block, 0, H, n_recent, kf, kb,
+                                     offset, chunk)
+    torch.cuda.synchronize()
+    ref = _oracle_hsa_rows(q, k, P, block, offset, chunk, range(H), n_recent, kf, kb)
+    _check_lists(idx, cnt, ref, idx.shape[3])

@@ -68,7 +68,8 @@ def test_noalloc_matches_workspace_entry_point_twice():
 
 
 def test_noalloc_near_the_scratch_limit_and_beyond():
-    # 24 heads x (126 + 126 pooled rows) x 128 x 8 B = 6.2 MB of the 16 MiB
+    # 24 heads x (126 + 126) pooled sums of 128 float64, plus one 64-row piece
+    # per group and frame (128 float64 partials + 2 keys): 12.4 MB of the 16 MiB
     B, H, T, P, D = 1, 24, 126, 64, 128
     g = torch.Generator(device=DEV).manual_seed(22)
     q = torch.randn((B, H, T * P, D), generator=g, device=DEV).to(torch.bfloat16)
