@@ -26,6 +26,7 @@ SOURCES = [
     "attn_api.cpp",
     "cag.cpp",
     "frame_sets.hip",
+    "frame_sets_host.cpp",
     "merge.hip",
     "topk.hip",
     "hsa.hip",
