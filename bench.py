@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
+SPIN_CYCLES = 20_000_000    # a few milliseconds of GPU spin before a timed batch
 METRIC = "effective attention TFLOP/s (attended pairs) + % of bf16 MFMA peak, 1 GPU"
 KERNEL_SOURCES = ["frame_sparse_attention_amd/csrc/attn_bf16.hip",
                   "frame_sparse_attention_amd/csrc/attn_common.h"]
@@ -146,44 +147,55 @@ def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float, o_gpu=None, lse_gpu=None
     return out
 
 
+def _tiles_of_runs(frames, P, tile_keys):
+    """64-key tiles the kernel walks over the runs of consecutive frames of a
+    list; a run starts on the 8-key boundary at or below its first key."""
+    tiles = 0
+    start = prev = None
+    for f in list(frames) + [None]:
+        if prev is not None and f == prev + 1:
+            prev = f
+            continue
+        if prev is not None:
+            lo = (start * P) & ~7
+            tiles += -(-((prev + 1) * P - lo) // tile_keys)
+        start = prev = f
+    return tiles
+
+
 def issued_mfma(idx, cnt, P: int, D: int, rows_per_wave: int = 32, tile_keys: int = 64) -> int:
     """32x32x16 MFMA instructions the attention kernel issues for frame lists
     idx/cnt (numpy, [B,H,Tq,cap] / [B,H,Tq]) with one block per 128-row tile of
     a query frame: every wavefront whose first row lies inside the frame
     (ceil(P/32) of them per frame) walks every 64-key tile of every run of
-    consecutive listed frames (a run starts on the 8-key boundary at or below
-    its first key) and issues D/16 x 2 Q.K^T and D/32 x 4 P.V MFMAs per tile,
-    plus the Q.K^T of one tile past the last (computed, never used)."""
-    waves = -(-P // rows_per_wave)
+    consecutive listed frames and issues D/16 x 2 Q.K^T and D/32 x 4 P.V MFMAs
+    per tile, plus the Q.K^T of one tile past the last (computed, never used)."""
     qk, pv = 2 * (D // 16), 4 * (D // 32)
+    waves = -(-P // rows_per_wave)
     total = 0
     B, H, Tq, _ = idx.shape
     for b in range(B):
         for h in range(H):
             for t in range(Tq):
-                lst = idx[b, h, t, :cnt[b, h, t]]
-                if lst.size == 0:
-                    continue
-                tiles = 0
-                start = prev = int(lst[0])
-                for f in list(lst[1:].tolist()) + [None]:
-                    if f is not None and f == prev + 1:
-                        prev = f
-                        continue
-                    lo = (start * P) & ~7
-                    tiles += -(-((prev + 1) * P - lo) // tile_keys)
-                    if f is not None:
-                        start = prev = f
-                total += waves * (tiles * (qk + pv) + qk)
+                tiles = _tiles_of_runs([int(f) for f in idx[b, h, t, :cnt[b, h, t]]], P,
+                                       tile_keys)
+                if tiles:
+                    total += waves * (tiles * (qk + pv) + qk)
     return int(total)
 
 
 def time_ms(fn, reps: int = 20) -> float:
-    """Average duration of fn() over reps launches, HIP events on the current stream."""
+    """Average GPU duration of fn() over reps back-to-back launches: HIP events
+    on the current stream around them.  The stream first runs a short spin
+    kernel, so that the host has enqueued every launch before the first one
+    starts: the events then see the kernels' own time, not the host's
+    argument checks between launches."""
     import torch
     fn()
+    torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(SPIN_CYCLES)
     e0.record(st)
     for _ in range(reps):
         fn()
@@ -328,25 +340,6 @@ def aux_rows(dev):
         "effective_TFLOP_per_s": round(4 * hw.D * hpairs / (ms_hattn * 1e-3) / 1e12, 1)}
     del q, k, qd, kd, v, prep, idx, cnt, hidx, hcnt
     out["cag_rollout"] = rollout_row(dev)
-    # the long-video workload (H24, 126 frames x 3600 tokens, C33 W11 T_per8), one
-    # step: inputs drawn on the device (same shape and distribution; the seeded
-    # CPU recipe of the parity tests would take minutes at this size)
-    lv = wl.long_video()
-    gen = torch.Generator(device=dev).manual_seed(lv.seed)
-    qv, kv_, vv = (torch.randn((lv.B, lv.H, lv.Nq, lv.D), generator=gen, device=dev,
-                               dtype=torch.float32).to(torch.bfloat16) for _ in range(3))
-    lidx, lcnt = fsa.build_frame_sets(lv.policies, lv.B, lv.Tq, lv.Tk, device=dev)
-    lprep = fsa.prepare_values(vv)
-    lo_, ll_ = fsa.sparse_frame_attn_prepared(qv, kv_, lprep, lidx, lcnt, lv.P)
-    ms_lv = time_ms(lambda: fsa.sparse_frame_attn_prepared(qv, kv_, lprep, lidx, lcnt, lv.P,
-                                                           out=lo_, out_lse=ll_), 3)
-    lpairs = int(lcnt.to(torch.int64).sum()) * lv.P * lv.P
-    out["long_video_step"] = {
-        "workload": lv.name, "ms_attention": round(ms_lv, 2), "attended_pairs": lpairs,
-        "effective_TFLOP_per_s": round(4 * lv.D * lpairs / (ms_lv * 1e-3) / 1e12, 1),
-        "pct_bf16_peak": round(100 * 4 * lv.D * lpairs / (ms_lv * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
-    del qv, kv_, vv, lprep, lo_, ll_, lidx, lcnt
-    torch.cuda.empty_cache()
     # chunk-aware growth schedule of a 60-chunk rollout (host code: a schedule
     # step before each chunk's list building)
     import time as _time
@@ -404,6 +397,27 @@ def aux_rows(dev):
                         "ms_two_branches_plus_merge": round(ms_three, 4),
                         "ms_union_only": round(ms_union, 4),
                         "effective_TFLOP_per_s": round(4 * d.D * pairs / (ms_dual * 1e-3) / 1e12, 1)}
+    del q, k, v, lists, prep
+    torch.cuda.empty_cache()
+    # the long-video workload (H24, 126 frames x 3600 tokens, C33 W11 T_per8), one
+    # step: inputs drawn on the device (same shape and distribution; the seeded
+    # CPU recipe of the parity tests would take minutes at this size)
+    lv = wl.long_video()
+    gen = torch.Generator(device=dev).manual_seed(lv.seed)
+    qv, kv_, vv = (torch.randn((lv.B, lv.H, lv.Nq, lv.D), generator=gen, device=dev,
+                               dtype=torch.float32).to(torch.bfloat16) for _ in range(3))
+    lidx, lcnt = fsa.build_frame_sets(lv.policies, lv.B, lv.Tq, lv.Tk, device=dev)
+    lprep = fsa.prepare_values(vv)
+    lo_, ll_ = fsa.sparse_frame_attn_prepared(qv, kv_, lprep, lidx, lcnt, lv.P)
+    ms_lv = time_ms(lambda: fsa.sparse_frame_attn_prepared(qv, kv_, lprep, lidx, lcnt, lv.P,
+                                                           out=lo_, out_lse=ll_), 3)
+    lpairs = int(lcnt.to(torch.int64).sum()) * lv.P * lv.P
+    out["long_video_step"] = {
+        "workload": lv.name, "ms_attention": round(ms_lv, 2), "attended_pairs": lpairs,
+        "effective_TFLOP_per_s": round(4 * lv.D * lpairs / (ms_lv * 1e-3) / 1e12, 1),
+        "pct_bf16_peak": round(100 * 4 * lv.D * lpairs / (ms_lv * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del qv, kv_, vv, lprep, lo_, ll_, lidx, lcnt
+    torch.cuda.empty_cache()
     return out
 
 

@@ -11,12 +11,17 @@
 // even), so the results are reproducible bit for bit.
 //
 // One block per (b, h, slot, 128-row piece of the frame): slots [0, cap) are
-// the listed key frames, slots [cap, cap + Tq) the query frames.  The block
-// computes the frame's cos/sin table in LDS, then streams its rows, 8
-// channels (16 bytes of bf16, 32 of float32) per thread and step; 8-channel
-// units with no rotated pair are copied as they are.  HBM-bound: every
-// element of a listed frame is read and written once.
+// the listed key frames, slots [cap, cap + Tq) the query frames.  The host
+// passes cos and sin of each pair's frequency theta_i = base^(-2i/rot); the
+// block raises (cos theta_i, sin theta_i) to its integer position by complex
+// squaring in float64 (about log2(pos) products instead of a transcendental
+// call), then streams its rows, 8 channels (16 bytes of bf16, 32 of float32)
+// per thread and step with 8 steps in flight; 8-channel units with no rotated
+// pair are copied as they are.  HBM-bound: every element of a listed frame is
+// read and written once.
 #pragma clang fp contract(off)
+
+#include <cmath>
 
 #include "fsa_internal.h"
 
@@ -25,6 +30,13 @@ namespace {
 constexpr int kRopeThreads = 256;
 constexpr int kMaxRotPairs = 128;  // rot <= 256
 constexpr int kRopeRows = 128;     // token rows of one frame per block
+constexpr int kRopeUnroll = 8;     // 8-channel units in flight per thread
+
+// cos and sin of every pair's frequency, computed on the host
+struct RopeFreqs {
+  double c[kMaxRotPairs];
+  double s[kMaxRotPairs];
+};
 
 // the nearest bfloat16 (ties to even) of a double, as raw bits.  Results in
 // the normal bfloat16 range are rounded on the bit pattern: the 45 low
@@ -54,14 +66,36 @@ __device__ inline uint16_t bf16_bits_nearest(double x) {
   return (uint16_t)(__float_as_uint((float)r) >> 16);  // r is a bfloat16 value: exact
 }
 
-__device__ inline void load8(const uint16_t *p, double *x) {
-  const uint4 raw = *reinterpret_cast<const uint4 *>(p);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+// 8 consecutive channels as loaded: 16 bytes of bf16 or 32 of float32
+template <typename T>
+struct Chunk8 {
+  uint4 w[sizeof(T) == 2 ? 1 : 2];
+};
+template <typename T>
+__device__ inline Chunk8<T> load_chunk(const T *p) {
+  Chunk8<T> c;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(c.w) / 16); ++i) c.w[i] = reinterpret_cast<const uint4 *>(p)[i];
+  return c;
+}
+template <typename T>
+__device__ inline void store_chunk(T *p, const Chunk8<T> &c) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(c.w) / 16); ++i) reinterpret_cast<uint4 *>(p)[i] = c.w[i];
+}
+__device__ inline void widen8(const Chunk8<uint16_t> &c, double *x) {
+  const uint32_t w[4] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = (double)__uint_as_float(w[i] << 16);
     x[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
   }
+}
+__device__ inline void widen8(const Chunk8<float> &c, double *x) {
+  const uint32_t w[8] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w,
+                         c.w[1].x, c.w[1].y, c.w[1].z, c.w[1].w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (double)__uint_as_float(w[i]);
 }
 __device__ inline void store8(uint16_t *p, const double *y) {
   uint32_t w[4];
@@ -70,33 +104,39 @@ __device__ inline void store8(uint16_t *p, const double *y) {
     w[i] = (uint32_t)bf16_bits_nearest(y[2 * i]) | ((uint32_t)bf16_bits_nearest(y[2 * i + 1]) << 16);
   *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
-__device__ inline void load8(const float *p, double *x) {
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-  x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
-  x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
-}
+
 __device__ inline void store8(float *p, const double *y) {
   *reinterpret_cast<float4 *>(p) = make_float4((float)y[0], (float)y[1], (float)y[2], (float)y[3]);
   *reinterpret_cast<float4 *>(p + 4) =
       make_float4((float)y[4], (float)y[5], (float)y[6], (float)y[7]);
 }
 
-__device__ inline void copy8(const uint16_t *p, uint16_t *q) {
-  *reinterpret_cast<uint4 *>(q) = *reinterpret_cast<const uint4 *>(p);
-}
-__device__ inline void copy8(const float *p, float *q) {
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-  *reinterpret_cast<float4 *>(q) = a;
-  *reinterpret_cast<float4 *>(q + 4) = b;
+
+// (cos p x, sin p x) from (cos x, sin x) for an integer p >= 0, by binary
+// powers of the unit complex number; each product is rounded (contraction is
+// off), and the result is within a few units in the last place of float64.
+__device__ inline void cis_power(double c1, double s1, int p, double *c, double *s) {
+  double rc = 1.0, rs = 0.0, bc = c1, bs = s1;
+  while (p > 0) {
+    if (p & 1) {
+      const double a = rc * bc, b = rs * bs, e = rc * bs, f = rs * bc;
+      rc = a - b;
+      rs = e + f;
+    }
+    const double a = bc * bc, b = bs * bs, e = bc * bs;
+    bc = a - b;
+    bs = e + e;
+    p >>= 1;
+  }
+  *c = rc;
+  *s = rs;
 }
 
 template <typename T>
 __global__ void __launch_bounds__(kRopeThreads) rope_reencode_kernel(
     const T *q, const T *k, T *qo, T *ko,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, int cap, int Nq, int Nk,
-    int D, int P, int Tk, int offset, int rot, double base, int slots, int row_blocks) {
+    int D, int P, int Tk, int offset, int rot, RopeFreqs freqs, int slots, int row_blocks) {
   __shared__ double s_cos[kMaxRotPairs], s_sin[kMaxRotPairs];
   __shared__ int s_pos;
   const int tid = threadIdx.x;
@@ -126,11 +166,11 @@ __global__ void __launch_bounds__(kRopeThreads) rope_reencode_kernel(
     dst = qo + (bh * Nq + (long long)tq * P) * D;
   }
   __syncthreads();
-  const double pos = (double)s_pos;
   for (int i = tid; i < rot / 2; i += kRopeThreads) {
-    const double ang = pos * pow(base, (-2.0 * i) / rot);
-    s_cos[i] = cos(ang);
-    s_sin[i] = sin(ang);
+    double c, sn;
+    cis_power(freqs.c[i], freqs.s[i], s_pos, &c, &sn);
+    s_cos[i] = c;
+    s_sin[i] = sn;
   }
   __syncthreads();
   const int per_row = D / 8;
@@ -138,30 +178,41 @@ __global__ void __launch_bounds__(kRopeThreads) rope_reencode_kernel(
   const int rows = P - row0 < kRopeRows ? P - row0 : kRopeRows;
   const int units = rows * per_row;
   const int rot_units = (rot + 7) / 8;  // 8-channel units holding rotated pairs
-  for (int u = tid; u < units; u += kRopeThreads) {
-    const int row = row0 + u / per_row, c0 = (u % per_row) * 8;
-    const long long off = (long long)row * D + c0;
-    if (u % per_row >= rot_units) {  // no rotated channel: the 16 or 32 bytes move as they are
-      copy8(src + off, dst + off);
-      continue;
-    }
-    double x[8], y[8];
-    load8(src + off, x);
+  for (int u0 = tid; u0 < units; u0 += kRopeUnroll * kRopeThreads) {
+    Chunk8<T> x[kRopeUnroll];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int pr = c0 / 2 + j;
-      if (2 * pr < rot) {
-        const double c = s_cos[pr], s = s_sin[pr];
-        const double a0 = x[2 * j] * c, a1 = x[2 * j + 1] * s;
-        const double b0 = x[2 * j] * s, b1 = x[2 * j + 1] * c;
-        y[2 * j] = a0 - a1;
-        y[2 * j + 1] = b0 + b1;
-      } else {
-        y[2 * j] = x[2 * j];
-        y[2 * j + 1] = x[2 * j + 1];
-      }
+    for (int i = 0; i < kRopeUnroll; ++i) {
+      const int u = u0 + i * kRopeThreads;
+      if (u < units) x[i] = load_chunk(src + (long long)(row0 + u / per_row) * D + (u % per_row) * 8);
     }
-    store8(dst + off, y);
+#pragma unroll
+    for (int i = 0; i < kRopeUnroll; ++i) {
+      const int u = u0 + i * kRopeThreads;
+      if (u >= units) continue;
+      const long long off = (long long)(row0 + u / per_row) * D + (u % per_row) * 8;
+      const int c0 = (u % per_row) * 8;
+      if (u % per_row >= rot_units) {  // no rotated channel: the bytes move as they are
+        store_chunk(dst + off, x[i]);
+        continue;
+      }
+      double v[8], y[8];
+      widen8(x[i], v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pr = c0 / 2 + j;
+        if (2 * pr < rot) {
+          const double c = s_cos[pr], s = s_sin[pr];
+          const double a0 = v[2 * j] * c, a1 = v[2 * j + 1] * s;
+          const double b0 = v[2 * j] * s, b1 = v[2 * j + 1] * c;
+          y[2 * j] = a0 - a1;
+          y[2 * j + 1] = b0 + b1;
+        } else {
+          y[2 * j] = v[2 * j];
+          y[2 * j + 1] = v[2 * j + 1];
+        }
+      }
+      store8(dst + off, y);
+    }
   }
 }
 
@@ -197,16 +248,23 @@ extern "C" fsa_status fsa_rope_reencode(const void *q, const void *k, int32_t dt
   FSA_REQUIRE((align & 15u) == 0, FSA_E_ARG, "q, k, q_out and k_out must be 16-byte aligned");
   FSA_REQUIRE(blocks < (1LL << 31) && slots < (1LL << 30), FSA_E_SHAPE,
               "too many frames (%lld blocks)", blocks);
+  // theta_i = base^(-2i/rot) and its cos / sin, in float64 on the host
+  RopeFreqs freqs{};
+  for (int i = 0; i < rot / 2; ++i) {
+    const double th = std::pow(base, (-2.0 * i) / rot);
+    freqs.c[i] = std::cos(th);
+    freqs.s[i] = std::sin(th);
+  }
   hipStream_t s = fsa::as_stream(stream);
   if (dt == FSA_BF16)
     hipLaunchKernelGGL(rope_reencode_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kRopeThreads),
                        0, s, static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<uint16_t *>(q_out), static_cast<uint16_t *>(k_out), idx, cnt,
-                       cap, Nq, Nk, D, P, Tk, q_kv_offset, rot, base, (int)slots, row_blocks);
+                       cap, Nq, Nk, D, P, Tk, q_kv_offset, rot, freqs, (int)slots, row_blocks);
   else
     hipLaunchKernelGGL(rope_reencode_kernel<float>, dim3((unsigned)blocks), dim3(kRopeThreads), 0,
                        s, static_cast<const float *>(q), static_cast<const float *>(k),
                        static_cast<float *>(q_out), static_cast<float *>(k_out), idx, cnt, cap,
-                       Nq, Nk, D, P, Tk, q_kv_offset, rot, base, (int)slots, row_blocks);
+                       Nq, Nk, D, P, Tk, q_kv_offset, rot, freqs, (int)slots, row_blocks);
   return fsa::check_launch("rope_reencode");
 }

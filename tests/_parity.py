@@ -45,6 +45,30 @@ def oracle_rows(q, k, v, idx, cnt, P, rows, heads=None, scale=None):
     return O, L
 
 
+def oracle_whole_frames(q, k, v, idx, cnt, P, b, h, frames, threads=8, scale=None):
+    """Oracle O [len(frames)*P, D] and LSE [len(frames)*P] of every row of the
+    given query frames of head (b, h): the oracle's own masked attention,
+    frame by frame, with the frames spread over a thread pool (numpy releases
+    the interpreter lock in its BLAS and elementwise kernels)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    idx = idx.cpu().numpy() if torch.is_tensor(idx) else idx
+    cnt = cnt.cpu().numpy() if torch.is_tensor(cnt) else cnt
+    k64 = k[b, h].double().numpy()
+    v64 = v[b, h].double().numpy()
+    Tk = k64.shape[0] // P
+    scale = 1.0 / np.sqrt(q.shape[3]) if scale is None else scale
+
+    def one(t):
+        mask = oatt.token_mask(idx[b, h, t, :cnt[b, h, t]], Tk, P)
+        return oatt.attend_rows(q[b, h, t * P:(t + 1) * P].double().numpy(), k64, v64, mask,
+                                scale)
+
+    with ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(one, list(frames)))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
 def assert_close(o, lse, o_ref, lse_ref, kind: str, what: str = ""):
     """max|dO| and max|dLSE| within the tolerance; -inf LSE must match exactly."""
     to, tl = TOL[kind]

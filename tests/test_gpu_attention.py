@@ -134,6 +134,34 @@ def test_malformed_entries_are_skipped_not_read():
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_neighbouring_frames_with_unrelated_lists(D):
+    # P = 150 (a 128-row tile and a 22-row tail per frame): neighbouring query
+    # frames whose lists are disjoint, empty, identical, subset / superset or
+    # interleaved, on heads of different kinds; every row against the oracle.
+    B, H, T, P = 1, 4, 5, 150
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s, outliers=2) for s in (71, 72, 73))
+    lists = [[[[0], [3], [], [1, 2, 3, 4], [2]],           # disjoint, empty, superset, subset
+              [[0, 1], [0, 1], [0, 1], [4], [0, 2, 4]],    # identical, then disjoint, interleaved
+              [[1, 3], [0, 2, 4], [1, 3], [0, 2, 4], []],  # interleaved, last frame empty
+              [[4], [3, 4], [2, 3, 4], [1, 2, 3, 4], [0, 1, 2, 3, 4]]]]
+    idx, cnt = _lists_to_arrays(lists, B, H)
+    _run_and_check(q, k, v, idx, cnt, P, "bf16", f"neighbouring frames' lists D={D}")
+    # out-of-range entries are skipped: the result equals the lists without them
+    bad = idx.clone()
+    bad[0, 0, 1, 1] = 99                     # frame 1: [3, 99]
+    cnt_bad = cnt.clone()
+    cnt_bad[0, 0, 1] = 2
+    bad[0, 2, 2, 2] = -7                     # frame 2 of head 2: [1, 3, -7]
+    cnt_bad[0, 2, 2] = 3
+    _say(f"neighbouring lists with out-of-range entries D={D}")
+    o1, l1 = fsa.sparse_frame_attn(q.to(DEV), k.to(DEV), v.to(DEV), bad.to(DEV),
+                                   cnt_bad.to(DEV), P)
+    o2, l2 = fsa.sparse_frame_attn(q.to(DEV), k.to(DEV), v.to(DEV), idx.to(DEV), cnt.to(DEV), P)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_empty_sets_give_zero_and_minus_inf():
     B, H, T, P, D = 1, 2, 2, 33, 128
     q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s) for s in (16, 17, 18))

@@ -13,7 +13,7 @@ from oracle import frame_sets as ofs
 from oracle import merge as omerge
 from oracle import topk as otopk
 
-from _parity import assert_close, oracle_rows, sample_rows
+from _parity import assert_close, oracle_rows, oracle_whole_frames, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -133,19 +133,60 @@ def _long_video_inputs():
 
 @pytest.mark.parametrize("s", range(8))
 def test_long_video_sampled_rows(s):
-    # the full denoising sweep: every step's rotated anchors
+    # the full denoising sweep: every step's rotated anchors.  Step 0 is checked
+    # on every (head, query frame): 8 rows of each frame, always including the
+    # tile-edge rows 0, 127, 128 and P-1; the other steps on a sample of frames
+    # and heads.
     w = wl.long_video(s)
     q, k, v = _long_video_inputs()
     _say(f"{w.name} step {s}")
     idx, cnt, o, lse = _attn(w, q.to(DEV), k.to(DEV), v.to(DEV), w.policies)
     oidx, ocnt = ofs.build(w.policies, w.B, w.Tq, w.Tk, cap=idx.shape[3])
     assert np.array_equal(idx.numpy(), oidx) and np.array_equal(cnt.numpy(), ocnt)
-    frames = [0, 1, 62, 63, 124, 125]
+    if s == 0:
+        frames, heads = range(w.Tq), list(range(w.H))
+    else:
+        frames, heads = [0, 1, 62, 63, 124, 125], [0, 7, 23]
     rows = sample_rows(w.P, frames, 8, seed=s)
-    heads = [0, 7, 23] if s else list(range(0, 24, 4))
+    if s == 0:
+        for t in range(w.Tq):
+            assert {t * w.P + p for p in (0, 127, 128, w.P - 1)} <= set(rows.tolist())
     o_ref, l_ref = oracle_rows(q, k, v, idx, cnt, w.P, rows, heads=heads)
     assert_close(o[:, heads][:, :, rows].cpu().numpy(), lse[:, heads][:, :, rows].cpu().numpy(),
                  o_ref, l_ref, "bf16", f"{w.name} step {s} ({rows.size} rows x {len(heads)} heads)")
+
+
+_LVSA = {}
+
+
+def _lvsa_step_output(s):
+    """The 42-frame LVSA workload's inputs and the GPU output of step s, in the
+    launch configuration the benchmark times (device lists, prepared values),
+    computed once per session."""
+    if s not in _LVSA:
+        w = wl.lvsa_shaped(s)
+        if "qkv" not in _LVSA:
+            _LVSA["qkv"] = wl.make_qkv(w)
+        q, k, v = _LVSA["qkv"]
+        qd, kd = q.to(DEV), k.to(DEV)
+        idx, cnt = fsa.build_frame_sets(w.policies, w.B, w.Tq, w.Tk, device=DEV)
+        prep = fsa.prepare_values(v.to(DEV))
+        o, lse = fsa.sparse_frame_attn_prepared(qd, kd, prep, idx, cnt, w.P)
+        torch.cuda.synchronize()
+        _LVSA[s] = (idx.cpu(), cnt.cpu(), o.cpu(), lse.cpu())
+    return _LVSA["qkv"], _LVSA[s]
+
+
+@pytest.mark.parametrize("h", range(12))
+def test_lvsa_step_every_row_against_oracle(h):
+    # every one of the 65520 query rows of head h, step 1, against the float64
+    # oracle (all 12 heads: the whole step, 786240 rows x 32760 keys each)
+    w = wl.lvsa_shaped(1)
+    (q, k, v), (idx, cnt, o, lse) = _lvsa_step_output(1)
+    _say(f"{w.name} step 1, head {h}: every row against the oracle")
+    o_ref, l_ref = oracle_whole_frames(q, k, v, idx, cnt, w.P, 0, h, range(w.Tq))
+    assert_close(o[0, h].numpy(), lse[0, h].numpy(), o_ref, l_ref, "bf16",
+                 f"{w.name} step 1 head {h} (all {w.Nq} rows)")
 
 
 def test_lvsa_every_row_bf16_path_against_fp32_path():
