@@ -15,10 +15,12 @@
 // passes cos and sin of each pair's frequency theta_i = base^(-2i/rot); the
 // block raises (cos theta_i, sin theta_i) to its integer position by complex
 // squaring in float64 (about log2(pos) products instead of a transcendental
-// call), then streams its rows, 8 channels (16 bytes of bf16, 32 of float32)
-// per thread and step with 8 steps in flight; 8-channel units with no rotated
-// pair are copied as they are.  HBM-bound: every element of a listed frame is
-// read and written once.
+// call).  A row is D/8 units of 8 channels (16 bytes of bf16, 32 of float32);
+// the ceil(rot/8) units holding rotated pairs and the units copied as they
+// are form two index spaces of their own, so every lane of a wavefront takes
+// the same path: first the copies (they need no table, so they stream while
+// it is built), then the rotations, 4 units in flight per thread.  HBM-bound:
+// every element of a listed frame is read and written once.
 #pragma clang fp contract(off)
 
 #include <cmath>
@@ -30,7 +32,7 @@ namespace {
 constexpr int kRopeThreads = 256;
 constexpr int kMaxRotPairs = 128;  // rot <= 256
 constexpr int kRopeRows = 128;     // token rows of one frame per block
-constexpr int kRopeUnroll = 8;     // 8-channel units in flight per thread
+constexpr int kRopeUnroll = 4;     // 8-channel units in flight per thread
 
 // cos and sin of every pair's frequency, computed on the host
 struct RopeFreqs {
@@ -97,12 +99,31 @@ __device__ inline void widen8(const Chunk8<float> &c, double *x) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = (double)__uint_as_float(w[i]);
 }
+__device__ inline bool bf16_normal(double x) {
+  const int ex = (int)(((unsigned long long)__double_as_longlong(x) >> 52) & 0x7FF) - 1023;
+  return ex >= -126 && ex <= 126;
+}
+__device__ inline uint32_t bf16_fast(double x) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const unsigned long long mag = b & 0x7FFFFFFFFFFFFFFFull;
+  const unsigned long long lsb = (mag >> 45) & 1ull;
+  const unsigned long long r = (mag + 0x0FFFFFFFFFFFull + lsb) >> 45;
+  return (uint32_t)(((b >> 48) & 0x8000u) | (unsigned int)(r - (896ull << 7)));
+}
 __device__ inline void store8(uint16_t *p, const double *y) {
-  uint32_t w[4];
+  uint32_t h[8];
+  bool all = true;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)bf16_bits_nearest(y[2 * i]) | ((uint32_t)bf16_bits_nearest(y[2 * i + 1]) << 16);
-  *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int i = 0; i < 8; ++i) {
+    h[i] = bf16_fast(y[i]);
+    all = all && bf16_normal(y[i]);
+  }
+  if (!all) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = bf16_bits_nearest(y[i]);
+  }
+  *reinterpret_cast<uint4 *>(p) =
+      make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
 __device__ inline void store8(float *p, const double *y) {
@@ -144,26 +165,58 @@ __global__ void __launch_bounds__(kRopeThreads) rope_reencode_kernel(
   const int slot = (blockIdx.x / row_blocks) % slots;
   const long long bh = blockIdx.x / ((long long)row_blocks * slots);
   const int32_t *lst = idx + bh * cap;
+  // the list count and this slot's entry are requested together
   int n = cnt[bh];
+  const int f = slot < cap ? lst[slot] : 0;
   n = n < 0 ? 0 : (n > cap ? cap : n);
   const T *src;
   T *dst;
   if (slot < cap) {  // listed key frame: its rank is its slot
-    if (slot >= n) return;
-    const int f = lst[slot];
-    if (f < 0 || f >= Tk) return;
-    if (tid == 0) s_pos = slot;
+    if (slot >= n || f < 0 || f >= Tk) return;
     src = k + (bh * Nk + (long long)f * P) * D;
     dst = ko + (bh * Nk + (long long)f * P) * D;
-  } else {  // query frame tq: rank of KV frame offset + tq among the listed frames
-    const int tq = slot - cap;
-    if (tid == 0) {
+  } else {  // query frame tq = slot - cap
+    src = q + (bh * Nq + (long long)(slot - cap) * P) * D;
+    dst = qo + (bh * Nq + (long long)(slot - cap) * P) * D;
+  }
+  if (tid == 0) {
+    if (slot < cap) {
+      s_pos = slot;
+    } else {  // rank of KV frame offset + tq among the listed frames
       int before = 0;
-      for (int i = 0; i < n; ++i) before += lst[i] < offset + tq ? 1 : 0;
+      for (int i = 0; i < n; ++i) before += lst[i] < offset + (slot - cap) ? 1 : 0;
       s_pos = before;
     }
-    src = q + (bh * Nq + (long long)tq * P) * D;
-    dst = qo + (bh * Nq + (long long)tq * P) * D;
+  }
+  const int per_row = D / 8;
+  const int rot_units = (rot + 7) / 8;  // units 0 .. rot_units-1 of a row hold rotated pairs
+  const int copy_units = per_row - rot_units;
+  const int row0 = rb * kRopeRows;
+  const int rows = P - row0 < kRopeRows ? P - row0 : kRopeRows;
+  const T *sb = src + (long long)row0 * D;
+  T *db = dst + (long long)row0 * D;
+  // the first rotated units are requested before anything else
+  const int nrot = rows * rot_units;
+  Chunk8<T> xr[kRopeUnroll];
+#pragma unroll
+  for (int i = 0; i < kRopeUnroll; ++i) {
+    const int u = tid + i * kRopeThreads;
+    if (u < nrot) xr[i] = load_chunk(sb + (u / rot_units) * D + (u % rot_units) * 8);
+  }
+  // units without a rotated pair: the bytes move as they are
+  const int ncopy = rows * copy_units;
+  for (int u0 = tid; u0 < ncopy; u0 += kRopeUnroll * kRopeThreads) {
+    Chunk8<T> x[kRopeUnroll];
+#pragma unroll
+    for (int i = 0; i < kRopeUnroll; ++i) {
+      const int u = u0 + i * kRopeThreads;
+      if (u < ncopy) x[i] = load_chunk(sb + (u / copy_units) * D + (rot_units + u % copy_units) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kRopeUnroll; ++i) {
+      const int u = u0 + i * kRopeThreads;
+      if (u < ncopy) store_chunk(db + (u / copy_units) * D + (rot_units + u % copy_units) * 8, x[i]);
+    }
   }
   __syncthreads();
   for (int i = tid; i < rot / 2; i += kRopeThreads) {
@@ -173,28 +226,22 @@ __global__ void __launch_bounds__(kRopeThreads) rope_reencode_kernel(
     s_sin[i] = sn;
   }
   __syncthreads();
-  const int per_row = D / 8;
-  const int row0 = rb * kRopeRows;
-  const int rows = P - row0 < kRopeRows ? P - row0 : kRopeRows;
-  const int units = rows * per_row;
-  const int rot_units = (rot + 7) / 8;  // 8-channel units holding rotated pairs
-  for (int u0 = tid; u0 < units; u0 += kRopeUnroll * kRopeThreads) {
+  // units with rotated pairs
+  for (int u0 = tid; u0 < nrot; u0 += kRopeUnroll * kRopeThreads) {
     Chunk8<T> x[kRopeUnroll];
 #pragma unroll
     for (int i = 0; i < kRopeUnroll; ++i) {
       const int u = u0 + i * kRopeThreads;
-      if (u < units) x[i] = load_chunk(src + (long long)(row0 + u / per_row) * D + (u % per_row) * 8);
+      if (u0 == tid)
+        x[i] = xr[i];
+      else if (u < nrot)
+        x[i] = load_chunk(sb + (u / rot_units) * D + (u % rot_units) * 8);
     }
 #pragma unroll
     for (int i = 0; i < kRopeUnroll; ++i) {
       const int u = u0 + i * kRopeThreads;
-      if (u >= units) continue;
-      const long long off = (long long)(row0 + u / per_row) * D + (u % per_row) * 8;
-      const int c0 = (u % per_row) * 8;
-      if (u % per_row >= rot_units) {  // no rotated channel: the bytes move as they are
-        store_chunk(dst + off, x[i]);
-        continue;
-      }
+      if (u >= nrot) continue;
+      const int c0 = (u % rot_units) * 8;
       double v[8], y[8];
       widen8(x[i], v);
 #pragma unroll
@@ -211,7 +258,7 @@ __global__ void __launch_bounds__(kRopeThreads) rope_reencode_kernel(
           y[2 * j + 1] = v[2 * j + 1];
         }
       }
-      store8(dst + off, y);
+      store8(db + (u / rot_units) * D + c0, y);
     }
   }
 }
