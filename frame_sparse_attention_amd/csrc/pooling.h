@@ -60,13 +60,15 @@ struct SegFamily {
   long long count() const { return (long long)nheads * nseg; }  // per batch entry
 };
 
-// First row (in src) of segment `s` of family f for batch entry b, head slot hs.
-__device__ inline long long seg_first_row(const SegFamily &f, long long seg) {
-  const long long per_b = (long long)f.nheads * f.nseg;
-  const int b = (int)(seg / per_b);
-  const long long r = seg % per_b;
-  const int hs = (int)(r / f.nseg);
-  const int s = (int)(r % f.nseg);
+// First row (in src) of segment `seg` of family f (batch entry b, head slot
+// hs, segment s).  Segment and piece counts stay below 2^31 (the launches
+// check), so the index arithmetic is 32-bit; only the row offset is 64-bit.
+__device__ inline long long seg_first_row(const SegFamily &f, int seg) {
+  const int per_b = f.nheads * f.nseg;
+  const int b = seg / per_b;
+  const int r = seg - b * per_b;
+  const int hs = r / f.nseg;
+  const int s = r - hs * f.nseg;
   const long long head = (long long)b * f.H + f.h_begin + hs;
   return head * f.head_rows + f.row0 + (long long)s * f.seg_rows;
 }
@@ -142,12 +144,12 @@ __global__ void __launch_bounds__(kPoolThreads) pool_pieces_kernel(SegFamily fa,
   // partial per wavefront reaches LDS
   __shared__ double s_red[kPoolThreads * VEC];
   __shared__ uint32_t s_kmin, s_kmax;
-  long long pid = blockIdx.x;
+  int pid = (int)blockIdx.x;
   const bool in_a = pid < na;
   const SegFamily f = in_a ? fa : fb;
-  if (!in_a) pid -= na;
-  const long long seg = pid / f.pieces;
-  const int piece = (int)(pid % f.pieces);
+  if (!in_a) pid -= (int)na;
+  const int seg = pid / f.pieces;
+  const int piece = pid - seg * f.pieces;
   const int first = piece * f.piece_rows;
   const int nrows = min(f.piece_rows, f.seg_rows - first);
   const T *src =
@@ -218,7 +220,7 @@ __global__ void __launch_bounds__(kPoolThreads) pool_pieces_kernel(SegFamily fa,
     for (int e = 0; e < VEC; ++e) s_red[rg * D + u * VEC + e] = acc[e];
   }
   __syncthreads();
-  double *out = f.part + pid * (long long)D;
+  double *out = f.part + (long long)pid * D;
   // a segment of one piece is finished here: its exact sum, directly
   const bool direct = f.direct != nullptr && f.pieces == 1;
   const int mbits = sizeof(T) == 2 ? fsa_exact::kBf16Bits : fsa_exact::kF32Bits;
@@ -234,12 +236,12 @@ __global__ void __launch_bounds__(kPoolThreads) pool_pieces_kernel(SegFamily fa,
         for (int r = 0; r < nrows; ++r) acc.add(elem_bits<T>(src + (long long)r * D + d));
         s = acc.rounded();
       }
-      f.direct[seg * D + d] = s + 0.0;
+      f.direct[(long long)seg * D + d] = s + 0.0;
     }
   }
   if (t == 0) {
-    f.keys[2 * pid] = s_kmin;
-    f.keys[2 * pid + 1] = s_kmax;
+    f.keys[2LL * pid] = s_kmin;
+    f.keys[2LL * pid + 1] = s_kmax;
   }
 }
 
@@ -300,7 +302,8 @@ __global__ void __launch_bounds__(kFinalThreads) finalize_kernel(FinalFamily fa,
   }
   // the first pooled segment of this output segment: its rows and the next
   // group - 1 segments' rows are consecutive in memory
-  const T *src = static_cast<const T *>(f.src) + seg_first_row(f, sid * ff.group) * (long long)D;
+  const T *src =
+      static_cast<const T *>(f.src) + seg_first_row(f, (int)(sid * ff.group)) * (long long)D;
   for (int d = lane; d < D; d += kFinalThreads) {
     fsa_exact::ExactSum acc;
     acc.clear();
