@@ -11,7 +11,7 @@
 //       with 16-byte loads (8 per thread in flight), adds them in float64 and
 //       records the smallest and largest magnitude it saw.  Output per piece:
 //       D float64 partial sums and two magnitude keys.
-//   finalize_kernel  one wavefront per segment.  When the segment's magnitudes
+//   finalize_kernel  one block per segment.  When the segment's magnitudes
 //       span few enough binades (fsa_exact::exact_by_range), every float64
 //       partial sum above was exact, in any order, so the pieces' sums add up
 //       to the exact sum.  Otherwise the segment's rows are read again and
@@ -255,12 +255,15 @@ struct FinalFamily {
   long long count() const { return pooled.count() / group; }  // per batch entry
 };
 
-constexpr int kFinalThreads = 64;
+constexpr int kFinalThreads = 256;
+constexpr int kFinalBatch = 16;  // partials each thread requests together
 
 template <typename T>
 __global__ void __launch_bounds__(kFinalThreads) finalize_kernel(FinalFamily fa, FinalFamily fb,
                                                                  FinalFamily fc, long long na,
                                                                  long long nb, int D) {
+  __shared__ double s_part[kFinalThreads];
+  __shared__ uint32_t s_kmin, s_kmax;
   long long sid = blockIdx.x;
   const int which = sid < na ? 0 : (sid < na + nb ? 1 : 2);
   sid -= which == 0 ? 0 : (which == 1 ? na : na + nb);
@@ -269,9 +272,14 @@ __global__ void __launch_bounds__(kFinalThreads) finalize_kernel(FinalFamily fa,
   const int np = ff.group * f.pieces;             // pieces of this output segment
   const long long p0 = sid * np;
   const long long nrows = (long long)ff.group * f.seg_rows;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    s_kmin = fsa_exact::kKeyMinInit;
+    s_kmax = fsa_exact::kKeyMaxInit;
+  }
+  __syncthreads();
   uint32_t kmin = fsa_exact::kKeyMinInit, kmax = fsa_exact::kKeyMaxInit;
-  for (int p = lane; p < np; p += kFinalThreads) {
+  for (int p = t; p < np; p += kFinalThreads) {
     kmin = min(kmin, f.keys[2 * (p0 + p)]);
     kmax = max(kmax, f.keys[2 * (p0 + p) + 1]);
   }
@@ -279,24 +287,45 @@ __global__ void __launch_bounds__(kFinalThreads) finalize_kernel(FinalFamily fa,
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
   }
+  if (t % 64 == 0) {
+    atomicMin(&s_kmin, kmin);
+    atomicMax(&s_kmax, kmax);
+  }
+  __syncthreads();
   const int mbits = sizeof(T) == 2 ? fsa_exact::kBf16Bits : fsa_exact::kF32Bits;
   double *out = ff.out + sid * (long long)D;
-  if (fsa_exact::exact_by_range(kmin, kmax, nrows, mbits)) {
-    for (int d = lane; d < D; d += kFinalThreads) {
-      // every addition is exact here, so the partials are added as they come,
-      // eight loads in flight at a time
-      const double *pp = f.part + p0 * D + d;
+  if (fsa_exact::exact_by_range(s_kmin, s_kmax, nrows, mbits)) {
+    // Every addition is exact here, in any order: the pieces of a channel
+    // are shared out over `parts` threads, each requesting its partials
+    // together, and the threads' sums are added at the end.
+    const int parts = D <= kFinalThreads ? kFinalThreads / D : 1;
+    for (int d0 = 0; d0 < D; d0 += kFinalThreads) {
+      const int d = d0 + t % D, part = t / D;
       double s = 0.0;
-      int p = 0;
-      for (; p + 8 <= np; p += 8) {
-        double x[8];
+      if (part < parts && d < D) {
+        const double *pp = f.part + p0 * D + d;
+        for (int pb = part; pb < np; pb += parts * kFinalBatch) {
+          double x[kFinalBatch];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = pp[(long long)(p + i) * D];
+          for (int i = 0; i < kFinalBatch; ++i) {
+            const int p = pb + i * parts;
+            x[i] = p < np ? pp[(long long)p * D] : 0.0;
+          }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s = s + x[i];
+          for (int i = 0; i < kFinalBatch; ++i) s = s + x[i];
+        }
       }
-      for (; p < np; ++p) s = s + pp[(long long)p * D];
-      out[d] = s + 0.0;
+      if (parts > 1) {
+        s_part[t] = s;
+        __syncthreads();
+        if (t < D) {
+          s = 0.0;
+          for (int q = 0; q < parts; ++q) s = s + s_part[q * D + t];
+        }
+        __syncthreads();
+      }
+      if (t < D && d0 + t < D) out[d0 + t] = s + 0.0;
+      if (parts > 1) break;  // D <= kFinalThreads: one pass covered every channel
     }
     return;
   }
@@ -304,7 +333,7 @@ __global__ void __launch_bounds__(kFinalThreads) finalize_kernel(FinalFamily fa,
   // group - 1 segments' rows are consecutive in memory
   const T *src =
       static_cast<const T *>(f.src) + seg_first_row(f, (int)(sid * ff.group)) * (long long)D;
-  for (int d = lane; d < D; d += kFinalThreads) {
+  for (int d = t; d < D; d += kFinalThreads) {
     fsa_exact::ExactSum acc;
     acc.clear();
     for (long long r = 0; r < nrows; ++r) acc.add(elem_bits<T>(src + r * D + d));
