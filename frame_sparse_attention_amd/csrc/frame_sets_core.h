@@ -58,48 +58,80 @@ FSA_HD inline void lvsa_window(int T, int C, int W, int t_per, int r, int t,
   *hi_out = hi;
 }
 
-// Frame set of query frame tq under one policy.  Writes at most `cap`
-// entries to out (ascending), pads the rest of the row with -1 and returns the
-// number of frames written.  `sel` holds the group's selected frames (MEMORY
-// heads read the first pol.topk of them).
-FSA_HD inline int build_one(const fsa_head_policy &pol, int Tk, int offset,
-                                         int chunk, int tq, const int32_t *sel, int cap,
-                                         int32_t *out) {
-  int n = 0;
+// Membership test of the frame set of one query frame under one policy: the
+// set A(t) is the ascending list of frames f in [0, Tk) for which keep(f)
+// holds.  Built once per (policy, query frame); `sel` holds the group's
+// selected frames (MEMORY heads read the first pol.topk of them).
+struct FrameTest {
+  int kind;
+  int lo, hi;       // LVSA window, SINK_WINDOW window, MEMORY recent frames, RANGE bounds
+  int r, t_per;     // LVSA rotating anchors: f mod t_per == r
+  int n_sink;       // SINK_WINDOW sink frames 0 .. n_sink-1
+  const int32_t *sel;
+  int topk;
+};
+
+FSA_HD inline FrameTest frame_test(const fsa_head_policy &pol, int Tk, int offset, int chunk,
+                                   int tq, const int32_t *sel) {
+  FrameTest ft{};
+  ft.kind = pol.kind;
   const int e = offset + (tq / chunk + 1) * chunk - 1;  // last KV frame of tq's chunk
   switch (pol.kind) {
-    case FSA_POL_FULL:
-      for (int f = 0; f < Tk && n < cap; ++f) out[n++] = f;
+    case FSA_POL_LVSA:
+      ft.t_per = pol.t_per;
+      ft.r = pos_mod(pol.step, pol.t_per);
+      lvsa_window(Tk, pol.budget, pol.window, pol.t_per, ft.r, offset + tq, &ft.lo, &ft.hi);
       break;
-    case FSA_POL_LVSA: {
-      const int r = pos_mod(pol.step, pol.t_per);
-      int lo, hi;
-      lvsa_window(Tk, pol.budget, pol.window, pol.t_per, r, offset + tq, &lo, &hi);
-      for (int f = 0; f < Tk && n < cap; ++f)
-        if ((f >= lo && f <= hi) || pos_mod(f, pol.t_per) == r) out[n++] = f;
+    case FSA_POL_SINK_WINDOW:
+      ft.n_sink = pol.n_sink;
+      ft.lo = e - pol.window + 1;
+      ft.hi = e;
       break;
-    }
-    case FSA_POL_SINK_WINDOW: {
-      const int wlo = e - pol.window + 1;
-      for (int f = 0; f < Tk && n < cap; ++f)
-        if (f < pol.n_sink || (f >= wlo && f <= e)) out[n++] = f;
+    case FSA_POL_MEMORY:
+      ft.lo = e - pol.n_recent + 1;
+      ft.hi = e;
+      ft.sel = sel;
+      ft.topk = pol.topk;
       break;
-    }
-    case FSA_POL_MEMORY: {
-      const int rlo = e - pol.n_recent + 1;
-      for (int f = 0; f < Tk && n < cap; ++f) {
-        bool keep = f >= rlo && f <= e;
-        for (int j = 0; j < pol.topk && !keep; ++j) keep = sel[j] == f;
-        if (keep) out[n++] = f;
-      }
-      break;
-    }
     case FSA_POL_RANGE:
-      for (int f = pol.lo < 0 ? 0 : pol.lo; f <= pol.hi && f < Tk && n < cap; ++f) out[n++] = f;
+      ft.lo = pol.lo;
+      ft.hi = pol.hi;
       break;
     default:
       break;
   }
+  return ft;
+}
+
+FSA_HD inline bool keep_frame(const FrameTest &ft, int f) {
+  switch (ft.kind) {
+    case FSA_POL_FULL:
+      return true;
+    case FSA_POL_LVSA:
+      return (f >= ft.lo && f <= ft.hi) || pos_mod(f, ft.t_per) == ft.r;
+    case FSA_POL_SINK_WINDOW:
+      return f < ft.n_sink || (f >= ft.lo && f <= ft.hi);
+    case FSA_POL_MEMORY: {
+      bool keep = f >= ft.lo && f <= ft.hi;
+      for (int j = 0; j < ft.topk && !keep; ++j) keep = ft.sel[j] == f;
+      return keep;
+    }
+    case FSA_POL_RANGE:
+      return f >= ft.lo && f <= ft.hi;
+    default:
+      return false;
+  }
+}
+
+// Frame set of query frame tq under one policy, serially: writes at most
+// `cap` entries to out (ascending), pads the rest of the row with -1 and
+// returns the number of frames written.
+FSA_HD inline int build_one(const fsa_head_policy &pol, int Tk, int offset, int chunk, int tq,
+                            const int32_t *sel, int cap, int32_t *out) {
+  const FrameTest ft = frame_test(pol, Tk, offset, chunk, tq, sel);
+  int n = 0;
+  for (int f = 0; f < Tk && n < cap; ++f)
+    if (keep_frame(ft, f)) out[n++] = f;
   for (int j = n; j < cap; ++j) out[j] = -1;
   return n;
 }
