@@ -17,7 +17,8 @@
 //              every key block of the candidate frames
 //   finalize   exact query-block, key-block and key-frame sums (a frame's
 //              sum from the pieces of its blocks)
-//   select     one wavefront per (b, h, query block): frame scores, the kf
+//   select     one block per (b, h, query block), one thread per candidate
+//              up to 256: frame scores, the kf
 //              best by rank, block scores over the chosen frames, the kb best
 //              by rank, then the ascending list with the recent frames.
 #pragma clang fp contract(off)
@@ -28,7 +29,7 @@ namespace {
 
 constexpr int kMaxHsaCand = 4096;  // candidate frames, and candidate blocks per query block
 
-__global__ void __launch_bounds__(64) hsa_select_kernel(
+__global__ void __launch_bounds__(256) hsa_select_kernel(
     const double *__restrict__ qblk, const double *__restrict__ kblk,
     const double *__restrict__ kframe, int H, int D, int h_begin, int Hs, int Gq, int nb,
     int Fc, int offset, int chunk, int n_recent, int kf, int kb, int cap,
@@ -37,7 +38,7 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   __shared__ unsigned char s_taken[kMaxHsaCand];
   __shared__ int s_frames[kMaxHsaCand];
   __shared__ double qs[kMaxPoolD];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x, nt = blockDim.x;
   const int j = blockIdx.x % Gq;
   const int hs = (blockIdx.x / Gq) % Hs;
   const int b = blockIdx.x / (Gq * Hs);
@@ -46,12 +47,12 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   const int first_recent = e - n_recent + 1;  // candidates: frames 0 .. first_recent-1
   const long long bh = (long long)b * Hs + hs;
 
-  for (int d = lane; d < D; d += 64) qs[d] = qblk[(bh * Gq + j) * D + d];
+  for (int d = lane; d < D; d += nt) qs[d] = qblk[(bh * Gq + j) * D + d];
   __syncthreads();
 
   // level 1: frames
   const double *kf_base = kframe + bh * Fc * D;
-  for (int f = lane; f < first_recent; f += 64)
+  for (int f = lane; f < first_recent; f += nt)
     s_score[f] = nan_last(ordered_dot(qs, kf_base + (long long)f * D, D));
   __syncthreads();
   take_best(s_score, s_taken, first_recent, kf);
@@ -62,7 +63,7 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   // s_frames[c / nb] * nb + c % nb, so candidate order is block order
   const int nbc = kf * nb;
   const double *kb_base = kblk + bh * (long long)Fc * nb * D;
-  for (int c = lane; c < nbc; c += 64) {
+  for (int c = lane; c < nbc; c += nt) {
     const long long blk = (long long)s_frames[c / nb] * nb + c % nb;
     s_score[c] = nan_last(ordered_dot(qs, kb_base + blk * D, D));
   }
@@ -74,8 +75,8 @@ __global__ void __launch_bounds__(64) hsa_select_kernel(
   compact_taken(s_taken, nbc, kb,
                 [&](int pos, int c) { out[pos] = s_frames[c / nb] * nb + c % nb; });
   const int n_rec = n_recent * nb;
-  for (int r = lane; r < n_rec; r += 64) out[kb + r] = first_recent * nb + r;
-  for (int p = kb + n_rec + lane; p < cap; p += 64) out[p] = -1;
+  for (int r = lane; r < n_rec; r += nt) out[kb + r] = first_recent * nb + r;
+  for (int p = kb + n_rec + lane; p < cap; p += nt) out[p] = -1;
   if (lane == 0) cnt[row] = kb + n_rec;
 }
 
@@ -207,7 +208,10 @@ extern "C" fsa_status fsa_select_hsa_blocks(
   launch_finalize(dt, qf.pieces == 1 ? no_final() : FinalFamily{L.qf, 1, L.qblk},
                   kf.pieces == 1 ? no_final() : FinalFamily{L.kf, 1, L.kblk},
                   FinalFamily{L.kf, sh.nb, L.kframe}, B, D, s);
-  hipLaunchKernelGGL(hsa_select_kernel, dim3((unsigned)(B * Hs * sh.Gq)), dim3(64), 0, s,
+  // one thread per candidate of the larger level, in whole wavefronts, up to 256
+  const int most = sh.Fc > topk_frames * sh.nb ? sh.Fc : topk_frames * sh.nb;
+  const int threads = most > 192 ? 256 : (most + 63) / 64 * 64;
+  hipLaunchKernelGGL(hsa_select_kernel, dim3((unsigned)(B * Hs * sh.Gq)), dim3(threads), 0, s,
                      L.qblk, L.kblk, L.kframe, H, D, h_begin, Hs, sh.Gq, sh.nb, sh.Fc,
                      q_kv_offset, chunk, n_recent, topk_frames, topk_blocks, cap, idx, cnt);
   return fsa::check_launch("select_hsa_blocks");

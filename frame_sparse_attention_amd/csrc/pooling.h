@@ -475,14 +475,15 @@ __device__ inline bool score_before(double s1, int i1, double s2, int i2) {
 }
 
 // Marks in s_taken the k best of s_score[0..n) in (score desc, index asc)
-// order; one wavefront (64 threads), scores NaN-free, k <= n.  Up to 1024
-// candidates each lane counts, for its candidates, how many others come
-// first, and keeps those with fewer than k; beyond that, k rounds of a
-// wavefront argmax.  Both give the same set.
+// order; every thread of the block calls it (it holds block barriers), scores
+// NaN-free, k <= n.  Up to 1024 candidates each thread counts, for its
+// candidates, how many others come first, and keeps those with fewer than k;
+// beyond that, k rounds of an argmax by the first wavefront.  Both give the
+// same set.
 __device__ inline void take_best(const double *s_score, unsigned char *s_taken, int n, int k) {
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x, nt = blockDim.x;
   if (n <= 1024) {
-    for (int i = lane; i < n; i += 64) {
+    for (int i = t; i < n; i += nt) {
       const double si = s_score[i];
       int ahead = 0;
       for (int j = 0; j < n; ++j) ahead += score_before(s_score[j], j, si, i) ? 1 : 0;
@@ -491,37 +492,41 @@ __device__ inline void take_best(const double *s_score, unsigned char *s_taken, 
     __syncthreads();
     return;
   }
-  for (int i = lane; i < n; i += 64) s_taken[i] = 0;
+  for (int i = t; i < n; i += nt) s_taken[i] = 0;
   __syncthreads();
   for (int round = 0; round < k; ++round) {
-    double bs = 0.0;
-    int bi = -1;
-    for (int i = lane; i < n; i += 64) {
-      if (s_taken[i]) continue;
-      const double s = s_score[i];
-      if (bi < 0 || score_before(s, i, bs, bi)) {
-        bs = s;
-        bi = i;
+    if (t < 64) {
+      double bs = 0.0;
+      int bi = -1;
+      for (int i = t; i < n; i += 64) {
+        if (s_taken[i]) continue;
+        const double s = s_score[i];
+        if (bi < 0 || score_before(s, i, bs, bi)) {
+          bs = s;
+          bi = i;
+        }
       }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double os = __shfl_xor(bs, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi >= 0 && (bi < 0 || score_before(os, oi, bs, bi))) {
-        bs = os;
-        bi = oi;
+      for (int off = 32; off >= 1; off >>= 1) {
+        const double os = __shfl_xor(bs, off);
+        const int oi = __shfl_xor(bi, off);
+        if (oi >= 0 && (bi < 0 || score_before(os, oi, bs, bi))) {
+          bs = os;
+          bi = oi;
+        }
       }
+      if (t == 0) s_taken[bi] = 1;
     }
-    if (lane == 0) s_taken[bi] = 1;
     __syncthreads();
   }
 }
 
 // Calls emit(pos, i) for the indices i < n with s_taken[i] set, pos counting
-// them in ascending i, for pos < limit; one wavefront.
+// them in ascending i, for pos < limit; the first wavefront does it (threads
+// beyond it return at once).
 template <typename Emit>
 __device__ inline void compact_taken(const unsigned char *s_taken, int n, int limit, Emit emit) {
   const int lane = threadIdx.x;
+  if (lane >= 64) return;
   int count = 0;
   for (int base = 0; base < n; base += 64) {
     const int i = base + lane;
