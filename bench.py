@@ -147,6 +147,30 @@ def cpu_baseline(w, q, k, v, idx, cnt, budget_s: float, o_gpu=None, lse_gpu=None
     return out
 
 
+def long_video_parity(sample):
+    """The oracle on the sampled rows of the timed long-video output (rows at
+    tile edges of a few query frames of two heads), element by element."""
+    import numpy as np
+
+    from oracle import attention as oatt
+    max_do = max_dl = 0.0
+    n = 0
+    for s in sample:
+        kk, vv = s["k"].float().numpy(), s["v"].float().numpy()
+        per = len(s["rows"]) // len(s["frames"])
+        for i, lst in enumerate(s["lists"]):
+            sl = slice(i * per, (i + 1) * per)
+            mask = oatt.token_mask(lst, s["Tk"], s["P"])
+            o_ref, l_ref = oatt.attend_rows(s["q"][sl].numpy(), kk, vv, mask,
+                                            1.0 / np.sqrt(s["D"]))
+            max_do = max(max_do, float(np.max(np.abs(s["o"][sl].numpy() - o_ref))))
+            max_dl = max(max_dl, float(np.max(np.abs(s["lse"][sl].numpy() - l_ref))))
+            n += per
+    return {"heads": [s["h"] for s in sample], "rows": n, "max_abs_dO": max_do,
+            "max_abs_dLSE": max_dl, "tolerance": {"dO": 1e-2, "dLSE": 1e-3},
+            "ok": bool(max_do <= 1e-2 and max_dl <= 1e-3)}
+
+
 def _tiles_of_runs(frames, P, tile_keys):
     """64-key tiles the kernel walks over the runs of consecutive frames of a
     list; a run starts on the 8-key boundary at or below its first key."""
@@ -262,12 +286,14 @@ def rollout_row(dev):
             "effective_TFLOP_per_s": round(4 * w.D * total_pairs / (ms * 1e-3) / 1e12, 1)}
 
 
-def aux_rows(dev):
+def aux_rows(dev, sample=None):
     """The other hot-path rows at their workload shapes: frame pooling + top-k
     (AR chunk, memory heads 8-11) and the LSE merge against the HBM roof; the AR
     chunk's attention with frame-level and with two-level (frame, then block)
     memory heads, and its per-head rotary re-encoding (HBM roof); the
-    decomposable workload's single-pass dual output."""
+    decomposable workload's single-pass dual output.  With a list `sample`, rows
+    of the timed long-video output and the inputs they need are appended to it
+    for the CPU leg's oracle check."""
     import torch
 
     import frame_sparse_attention_amd as fsa
@@ -416,6 +442,18 @@ def aux_rows(dev):
         "workload": lv.name, "ms_attention": round(ms_lv, 2), "attended_pairs": lpairs,
         "effective_TFLOP_per_s": round(4 * lv.D * lpairs / (ms_lv * 1e-3) / 1e12, 1),
         "pct_bf16_peak": round(100 * 4 * lv.D * lpairs / (ms_lv * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    if sample is not None:
+        # rows at tile edges of a few query frames of two heads, with the timed
+        # output, for the CPU leg to check against the oracle
+        frames = [0, 40, 85, lv.Tq - 1]
+        edges = [0, 127, 128, lv.P - 1]
+        for h in (0, lv.H - 7):
+            rows = [t * lv.P + p for t in frames for p in edges]
+            sample.append({
+                "P": lv.P, "Tk": lv.Tk, "D": lv.D, "h": h, "frames": frames, "rows": rows,
+                "q": qv[0, h, rows].float().cpu(), "k": kv_[0, h].cpu(), "v": vv[0, h].cpu(),
+                "lists": [lidx[0, h, t, :int(lcnt[0, h, t])].cpu().tolist() for t in frames],
+                "o": lo_[0, h, rows].cpu(), "lse": ll_[0, h, rows].cpu()})
     del qv, kv_, vv, lprep, lo_, ll_, lidx, lcnt
     torch.cuda.empty_cache()
     return out
@@ -564,9 +602,10 @@ def main() -> int:
     }
     prep_bytes = w.B * w.H * w.Nk * w.D * 4        # read bf16 V, write fp16 copy
     out["kernels_GB_per_s"] = {"prepare_values": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)}
+    lv_sample = [] if args.cpu_seconds > 0 else None
     if not args.no_aux:
         print("[bench] top-k and merge rows", file=sys.stderr, flush=True)
-        out["aux"] = aux_rows(dev)
+        out["aux"] = aux_rows(dev, lv_sample)
     if args.cpu_seconds > 0:
         print("[bench] CPU baseline (oracle)", file=sys.stderr, flush=True)
         # the baseline uses the frame sets of step 0
@@ -575,6 +614,8 @@ def main() -> int:
         idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, idx_h, cnt_h, args.cpu_seconds,
                                            o.cpu(), lse.cpu())
+        if lv_sample:
+            out["cpu_baseline"]["parity_long_video_sampled"] = long_video_parity(lv_sample)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
