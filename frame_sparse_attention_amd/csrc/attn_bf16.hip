@@ -142,24 +142,39 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char s_v[2][VBYTES];
   __shared__ int s_lo[FSA_MAX_CAP], s_hi[FSA_MAX_CAP];
   __shared__ int s_nruns[2];
+  __shared__ int s_unequal;
   __shared__ int s_order[128];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, j = lane % 32, g = lane / 32;
 
-  int tile = xcd_logical_tile(blockIdx.x, gridDim.x);
-  const int qt = tile % qtiles;
-  tile /= qtiles;
-  const int sp = tile % splits;  // part of the list this block attends (DUAL: always 0 of 1)
-  tile /= splits;
-  const int tq = tile % Tq;
-  tile /= Tq;
-  // tile is now the head slot b * H + h; small grids visit heads in a
-  // cost-balanced order (at most 64 heads, at most 1024 blocks)
-  const int G = (int)(gridDim.x / ((unsigned)qtiles * splits * Tq));
-  if (gridDim.x <= 1024 && G <= 64)
-    tile = balanced_head(tile, G, Tq, la.cnt, la.cap, DUAL ? lb.cnt : nullptr, lb.cap, s_order);
+  int tile, qt, sp, tq;
+  int lst;
+  // (D = 128: two blocks per CU; the D = 64 kernel fits three, other pairs)
+  if (D == 128 && splits == 1 && gridDim.x > 256 && gridDim.x <= 512 &&
+      paired_list_tile(blockIdx.x, qtiles, (int)(gridDim.x / (unsigned)qtiles), la.cnt, la.cap,
+                       DUAL ? lb.cnt : nullptr, lb.cap, reinterpret_cast<int *>(&s_k[0][0]),
+                       &s_unequal, &lst, &qt)) {
+    // all blocks resident at once and lists of unequal cost: heavy blocks on CUs
+    // of their own or next to light ones
+    sp = 0;
+    tq = lst % Tq;
+    tile = lst / Tq;
+  } else {
+    tile = xcd_logical_tile(blockIdx.x, gridDim.x);
+    qt = tile % qtiles;
+    tile /= qtiles;
+    sp = tile % splits;  // part of the list this block attends (DUAL: always 0 of 1)
+    tile /= splits;
+    tq = tile % Tq;
+    tile /= Tq;
+    // tile is now the head slot b * H + h; small grids visit heads in a
+    // cost-balanced order (at most 64 heads, at most 1024 blocks)
+    const int G = (int)(gridDim.x / ((unsigned)qtiles * splits * Tq));
+    if (gridDim.x <= 1024 && G <= 64)
+      tile = balanced_head(tile, G, Tq, la.cnt, la.cap, DUAL ? lb.cnt : nullptr, lb.cap, s_order);
+  }
   const int h = tile % H;
   const int b = tile / H;
   const long long head = (long long)b * H + h;

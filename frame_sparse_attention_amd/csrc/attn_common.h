@@ -108,4 +108,63 @@ __device__ inline int balanced_head(int slot, int G, int Tq, const int32_t *cnt_
   return s_tmp[64 + slot];
 }
 
+// Block order for grids of 257 to 512 blocks, which are resident all at once
+// at two blocks per CU.  On an MI355X the blocks of one XCD (local index
+// k = bid / 8) land so that k and k + 32 share a CU and k < 32 without such
+// a partner runs alone (measured with the hardware's CU ids).  A CU then runs
+// until its longer block ends, and that block speeds up once its partner is
+// done.  The blocks are ranked by the cost of their list, heaviest first; the
+// 32 heaviest of the first 256 go to XCD 0, the next 32 to XCD 1, and so on,
+// the heaviest of each XCD's share to its unpartnered slots.  The remaining
+// blocks, the lightest, fill the partner slots, lightest paired with
+// heaviest, the lightest share on XCD 0.  Each XCD holds two contiguous
+// ranges of the ranking, so the query tiles of one list mostly share an L2.
+// Needs L <= 2 * blockDim.x lists (L * qtiles = gridDim.x blocks) and 2 * L
+// LDS ints at `s_tmp`; returns false (and leaves the outputs) when every
+// list costs the same, where the contiguous order is better.
+__device__ inline bool paired_list_tile(int bid, int qtiles, int L, const int32_t *cnt_a,
+                                        int cap_a, const int32_t *cnt_b, int cap_b, int *s_tmp,
+                                        int *s_flag, int *list_out, int *qt_out) {
+  constexpr int kXcd = 8, kSlots = 32;  // CUs per XCD
+  const int nt = blockDim.x;
+  if (threadIdx.x == 0) *s_flag = 0;
+  for (int l = threadIdx.x; l < L; l += nt) {
+    int n = cnt_a[l];
+    int c = n < 0 ? 0 : (n > cap_a ? cap_a : n);
+    if (cnt_b != nullptr) {
+      n = cnt_b[l];
+      c += n < 0 ? 0 : (n > cap_b ? cap_b : n);
+    }
+    s_tmp[l] = c;
+  }
+  __syncthreads();
+  for (int l = threadIdx.x; l < L; l += nt) {
+    const int c = s_tmp[l];
+    int rank = 0;
+    bool equal = true;
+    for (int j = 0; j < L; ++j) {
+      const int cj = s_tmp[j];
+      rank += (cj > c || (cj == c && j < l)) ? 1 : 0;
+      equal = equal && cj == c;
+    }
+    s_tmp[L + rank] = l;
+    if (!equal) *s_flag = 1;
+  }
+  __syncthreads();
+  if (*s_flag == 0) return false;
+  const int N = L * qtiles;
+  const int xcd = bid % kXcd, k = bid / kXcd;
+  const int per = N / kXcd, rem = N % kXcd;
+  const int s_x = per + (xcd < rem ? 1 : 0) - kSlots;        // partnered slots of this XCD
+  const int p_x = xcd * (per - kSlots) + (xcd < rem ? xcd : rem);  // of the XCDs before it
+  int i;  // position of this block in the ranking
+  if (k < kSlots)
+    i = kSlots * xcd + (k >= s_x ? k - s_x : kSlots - s_x + k);
+  else
+    i = N - p_x - s_x + (s_x - 1 - (k - kSlots));
+  *list_out = s_tmp[L + i / qtiles];
+  *qt_out = i % qtiles;
+  return true;
+}
+
 }  // namespace fsa

@@ -268,6 +268,27 @@ def test_small_grids_visit_heads_in_cost_order(B, H, widths):
     assert_close(oab.cpu().numpy(), l_ab.cpu().numpy(), *ru, "bf16", f"cost order dual O_AB B={B}")
 
 
+@pytest.mark.parametrize("B,H,T,P", [(1, 1, 257, 8), (2, 4, 64, 16), (1, 4, 25, 300),
+                                     (1, 10, 17, 260)])
+def test_grids_resident_at_once_pair_heavy_with_light(B, H, T, P):
+    # Grids of 257 to 512 blocks (one per query tile) are resident at once, two
+    # per CU; with lists of unequal cost the kernel ranks the blocks and puts
+    # heavy ones on CUs of their own or next to light ones.  The cases take the
+    # ends of that range (257 and 512 blocks of one tile) and frames of three
+    # query tiles (300 and 510 blocks, the last tile ragged); frame t lists
+    # [t - w, t] with a seeded width w in 0..5 per (b, h, t).  Every row is
+    # checked against the oracle.
+    D = 128
+    rng = np.random.default_rng(B * 1000 + H * 100 + T)
+    q, k, v = (_rand((B, H, T * P, D), torch.bfloat16, s, outliers=2) for s in (81, 82, 83))
+    lists = [[[list(range(max(0, t - int(rng.integers(0, 6))), t + 1)) for t in range(T)]
+              for _ in range(H)] for _ in range(B)]
+    idx, cnt = _lists_to_arrays(lists, B, H)
+    blocks = B * H * T * -(-P // 128)
+    assert 256 < blocks <= 512
+    _run_and_check(q, k, v, idx, cnt, P, "bf16", f"resident grid of {blocks} blocks, P={P}")
+
+
 @pytest.mark.parametrize("kind,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
 def test_maximum_list_length_and_run_count(kind, D):
     # lists at the capacity limit (FSA_MAX_CAP = 1024 entries), a list of 512
