@@ -10,7 +10,7 @@
 // contraction off and is rounded once to the storage type (nearest, ties to
 // even), so the results are reproducible bit for bit.
 //
-// One block per (b, h, slot, 128-row piece of the frame): slots [0, cap) are
+// One block per (b, h, slot, 64-row piece of the frame): slots [0, cap) are
 // the listed key frames, slots [cap, cap + Tq) the query frames.  The host
 // passes cos and sin of each pair's frequency theta_i = base^(-2i/rot); the
 // block raises (cos theta_i, sin theta_i) to its integer position by complex
@@ -19,8 +19,10 @@
 // the ceil(rot/8) units holding rotated pairs and the units copied as they
 // are form two index spaces of their own, so every lane of a wavefront takes
 // the same path: first the copies (they need no table, so they stream while
-// it is built), then the rotations, 4 units in flight per thread.  HBM-bound:
-// every element of a listed frame is read and written once.
+// it is built), then the rotations.  With 64-row pieces a thread has all of
+// its units in flight at once for D = 128 (measured: 64-row pieces 21.9 us on
+// the AR chunk, 128-row 22.5, 256-row 26.4, 32-row 22.2).  HBM-bound: every
+// element of a listed frame is read and written once.
 #pragma clang fp contract(off)
 
 #include <cmath>
@@ -31,8 +33,9 @@ namespace {
 
 constexpr int kRopeThreads = 256;
 constexpr int kMaxRotPairs = 128;  // rot <= 256
-constexpr int kRopeRows = 128;     // token rows of one frame per block
-constexpr int kRopeUnroll = 4;     // 8-channel units in flight per thread
+constexpr int kRopeRows = 64;      // token rows of one frame per block
+constexpr int kRopeUnroll = 2;     // rotated 8-channel units in flight per thread
+constexpr int kCopyUnroll = 4;     // copied 8-channel units in flight per thread
 
 // cos and sin of every pair's frequency, computed on the host
 struct RopeFreqs {
@@ -179,13 +182,17 @@ __global__ void __launch_bounds__(kRopeThreads) rope_reencode_kernel(
     src = q + (bh * Nq + (long long)(slot - cap) * P) * D;
     dst = qo + (bh * Nq + (long long)(slot - cap) * P) * D;
   }
-  if (tid == 0) {
+  if (tid < 64) {
     if (slot < cap) {
-      s_pos = slot;
-    } else {  // rank of KV frame offset + tq among the listed frames
+      if (tid == 0) s_pos = slot;
+    } else {  // rank of KV frame offset + tq among the listed frames, 64 entries at a time
+      const int target = offset + (slot - cap);
       int before = 0;
-      for (int i = 0; i < n; ++i) before += lst[i] < offset + (slot - cap) ? 1 : 0;
-      s_pos = before;
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + tid;
+        before += __popcll(__ballot(i < n && lst[i] < target));
+      }
+      if (tid == 0) s_pos = before;
     }
   }
   const int per_row = D / 8;
@@ -205,15 +212,15 @@ __global__ void __launch_bounds__(kRopeThreads) rope_reencode_kernel(
   }
   // units without a rotated pair: the bytes move as they are
   const int ncopy = rows * copy_units;
-  for (int u0 = tid; u0 < ncopy; u0 += kRopeUnroll * kRopeThreads) {
-    Chunk8<T> x[kRopeUnroll];
+  for (int u0 = tid; u0 < ncopy; u0 += kCopyUnroll * kRopeThreads) {
+    Chunk8<T> x[kCopyUnroll];
 #pragma unroll
-    for (int i = 0; i < kRopeUnroll; ++i) {
+    for (int i = 0; i < kCopyUnroll; ++i) {
       const int u = u0 + i * kRopeThreads;
       if (u < ncopy) x[i] = load_chunk(sb + (u / copy_units) * D + (rot_units + u % copy_units) * 8);
     }
 #pragma unroll
-    for (int i = 0; i < kRopeUnroll; ++i) {
+    for (int i = 0; i < kCopyUnroll; ++i) {
       const int u = u0 + i * kRopeThreads;
       if (u < ncopy) store_chunk(db + (u / copy_units) * D + (rot_units + u % copy_units) * 8, x[i]);
     }
