@@ -159,8 +159,16 @@ def test_merge_lse_matches_oracle(rows, D):
         l1[2] = l2[2] = -float("inf")
         l1[3] = 80.0
         l2[3] = -80.0
+    # the operand of a zero weight may hold anything: NaN and inf there must
+    # not reach the output (the oracle gets the clean values, which carry no weight)
+    o1_dev, o2_dev = o1.clone(), o2.clone()
+    if rows >= 4:
+        o1_dev[0] = float("nan")
+        o2_dev[1] = float("inf")
+        o1_dev[2] = float("nan")
+        o2_dev[2] = -float("inf")
     _say(f"merge rows={rows} D={D}")
-    o, lse = fsa.merge_lse(o1.to(DEV), l1.to(DEV), o2.to(DEV), l2.to(DEV))
+    o, lse = fsa.merge_lse(o1_dev.to(DEV), l1.to(DEV), o2_dev.to(DEV), l2.to(DEV))
     torch.cuda.synchronize()
     n = min(rows, 3000)
     oo, ol = omerge.merge_lse(o1[:n].double().numpy(), l1[:n].double().numpy(),
