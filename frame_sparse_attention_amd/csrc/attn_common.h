@@ -119,9 +119,10 @@ __device__ inline int balanced_head(int slot, int G, int Tq, const int32_t *cnt_
 // blocks, the lightest, fill the partner slots, lightest paired with
 // heaviest, the lightest share on XCD 0.  Each XCD holds two contiguous
 // ranges of the ranking, so the query tiles of one list mostly share an L2.
-// Needs L <= 2 * blockDim.x lists (L * qtiles = gridDim.x blocks) and 2 * L
-// LDS ints at `s_tmp`; returns false (and leaves the outputs) when every
-// list costs the same, where the contiguous order is better.
+// L lists of qtiles blocks each make the N = L * qtiles blocks of the grid
+// (257 <= N <= 512); `s_tmp` holds 2 * L LDS ints and `s_flag` one.  Returns
+// false (and leaves the outputs) when every list costs the same, where the
+// contiguous order is better.
 __device__ inline bool paired_list_tile(int bid, int qtiles, int L, const int32_t *cnt_a,
                                         int cap_a, const int32_t *cnt_b, int cap_b, int *s_tmp,
                                         int *s_flag, int *list_out, int *qt_out) {
